@@ -1,0 +1,192 @@
+/*
+ * fp8attn.h — C-ABI of the online per-tensor FP8 attention library (libfp8attn.so).
+ *
+ * What the library computes, per attention call:
+ *   1. the absolute maximum of each of Q, K and V (one value per tensor),
+ *   2. a per-tensor E4M3 scale, from a 16-slot ring of observed maxima or from a
+ *      calibrated static maximum times a margin,
+ *   3. Q, K, V quantised to E4M3 with that scale, then a non-causal, variable-length
+ *      (cu_seqlens, no padding) flash-attention forward on FP8 matrix cores, or — when the
+ *      caller asks to skip FP8 for this call — the same attention in BF16.
+ *
+ * Sources for the behaviour (web pages):
+ *   - vLLM-Omni user guide "Quantized KV Cache", sections "Overview" (Q/K/V quantised on
+ *     the fly right before the attention operator, weights untouched; native dtype when
+ *     FP8 is not requested) and "Parameters" (step/layer selectors that keep listed
+ *     forwards in the native dtype).
+ *   - vLLM docs "FP8 ViT Encoder Attention", sections "Usage" (dynamic scaling driven by a
+ *     circular buffer of the last 16 observed Q/K/V amax values; static scales calibrated
+ *     once; saved scales multiplied by a margin that defaults to 1.5) and "Scale file format"
+ *     (one q/k/v triple per attention layer).
+ *   - the Korean wiki rewrite of that page, "FP8 ViT 인코더 어텐션", section "Requirements"
+ *     (the AMD backend is a varlen, per-tensor-scale FP8 flash attention).
+ * The E4M3 format is the OCP 8-bit floating point E4M3 ("FN") encoding: bias 7, no
+ * infinities, 0x7F/0xFF are NaN, largest finite magnitude 448.
+ *
+ * Conventions common to every call:
+ *   - Pointers are DEVICE pointers unless the name ends in _host.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream). Every call
+ *     only enqueues work on that stream and never waits for the device.
+ *   - The caller owns every buffer (state, workspace, inputs, outputs). The library
+ *     allocates no device memory and keeps no global state apart from the thread-local
+ *     error message.
+ *   - Argument checks happen on the host before anything is enqueued. A failed check
+ *     returns a negative status, enqueues nothing, and sets fp8attn_last_error().
+ *     A failed kernel launch returns FP8ATTN_EHIP.
+ *   - Tensors Q, K, V, O are packed "THD": [total_tokens][num_heads][head_dim], row major,
+ *     bf16, contiguous, sequences concatenated along tokens as described by cu_seqlens.
+ *   - cu_seqlens is int32[num_seqs + 1]: cu[0] = 0, non-decreasing, cu[num_seqs] = total
+ *     tokens. Empty sequences are allowed and produce no rows.
+ *   - Non-finite input values are outside the contract.
+ */
+#ifndef FP8ATTN_H
+#define FP8ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fp8attn_status {
+  FP8ATTN_OK = 0,
+  FP8ATTN_EINVAL = -1,      /* a null pointer, a size out of range, inconsistent cu_seqlens */
+  FP8ATTN_EUNSUPPORTED = -2, /* a valid request this build does not implement (head_dim != 128) */
+  FP8ATTN_EHIP = -3          /* the HIP runtime reported an error while enqueuing */
+} fp8attn_status;
+
+/* Scale modes of fp8attn_scales. */
+#define FP8ATTN_DYNAMIC 0 /* scale from the 16-slot ring of observed amax values */
+#define FP8ATTN_STATIC 1  /* scale from a calibrated amax times a margin */
+
+/* Flags of fp8attn_forward. */
+#define FP8ATTN_SKIP 1u /* run the BF16 kernel on the unquantised inputs; state is not read */
+
+#define FP8ATTN_RING_SLOTS 16
+#define FP8ATTN_E4M3_MAX 448.0f
+#define FP8ATTN_DEFAULT_MARGIN 1.5f
+
+/*
+ * Per-attention-layer scale state, in DEVICE memory, owned by the caller.
+ * The layout is part of the ABI so that callers can inspect, snapshot and restore it
+ * by copying bytes. Tensor index t: 0 = Q, 1 = K, 2 = V.
+ *   ring[t][s]   amax observed by dynamic forward number f is stored in slot f mod 16
+ *                (vLLM docs "FP8 ViT Encoder Attention", "Usage": 16 observed values).
+ *   cur[t]       fp32 bit image of the amax being gathered by fp8attn_observe_amax
+ *                (a non-negative float compares like its bit pattern); cleared by
+ *                fp8attn_scales.
+ *   count        number of dynamic scale updates so far (the next slot is count mod 16).
+ *   scale[t]     dequantisation scale A/448 of the current forward.
+ *   inv_scale[t] quantisation multiplier 448/A of the current forward.
+ *   amax[t]      the A behind scale[t] (window maximum, or static amax times margin).
+ */
+typedef struct fp8attn_state {
+  float ring[3][FP8ATTN_RING_SLOTS];
+  uint32_t cur[3];
+  uint32_t count;
+  float scale[3];
+  float inv_scale[3];
+  float amax[3];
+  uint32_t reserved[4];
+} fp8attn_state;
+
+/* Size in bytes of fp8attn_state (256). */
+size_t fp8attn_state_bytes(void);
+
+/*
+ * Zero a state (empty ring, count 0, no pending observation). Call once per attention
+ * layer before its first forward. Implemented with a kernel, not a memset node.
+ * Errors: EINVAL if state is NULL.
+ */
+int fp8attn_state_reset(void* state, void* stream);
+
+/*
+ * Observe the per-tensor absolute maximum of Q, K and V for this forward
+ * (vLLM docs "FP8 ViT Encoder Attention", "Usage": the amax of Q, K and V is observed on
+ * every dynamic forward). One launch reads all three bf16 tensors of n elements each
+ * (n = total_tokens * num_heads * head_dim; 16-byte aligned pointers) and folds
+ * max|x| into state->cur[t] with one atomic per block and tensor. The result is exact
+ * (a bf16 magnitude). n = 0 observes 0. Must be followed by exactly one fp8attn_scales.
+ * Errors: EINVAL for a NULL state, NULL tensor with n > 0, n < 0, or a misaligned pointer.
+ */
+int fp8attn_observe_amax(void* state, const void* q, const void* k, const void* v, int64_t n,
+                         void* stream);
+
+/*
+ * Compute this forward's scales (vLLM docs "FP8 ViT Encoder Attention", "Usage" and
+ * "Scale file format").
+ *   mode FP8ATTN_DYNAMIC: ring[t][count mod 16] = cur[t]; A_t = max over the 16 slots
+ *     (empty slots hold 0); count += 1. static_amax_host and margin are ignored.
+ *   mode FP8ATTN_STATIC: A_t = fp32(static_amax_host[t] * margin); the ring and count are
+ *     left unchanged. static_amax_host is a HOST array of 3 floats (q, k, v calibrated
+ *     amax); margin > 0 (the pages' default is 1.5, FP8ATTN_DEFAULT_MARGIN).
+ *   Both modes: A' = max(A_t, 2^-64); scale[t] = fp32(A'/448) and inv_scale[t] =
+ *     fp32(448/A'), each a correctly rounded division; cur[t] is cleared.
+ * One single-wave launch; no host synchronisation.
+ * Errors: EINVAL for a NULL state, an unknown mode, a NULL static_amax_host in static
+ * mode, a static amax that is negative or not finite, a margin that is not > 0 and finite.
+ */
+int fp8attn_scales(void* state, int mode, const float* static_amax_host, float margin,
+                   void* stream);
+
+/*
+ * Workspace needed by fp8attn_forward on the FP8 path, in bytes:
+ *   Q8 e4m3 [T][H][D] at offset 0,
+ *   K8 e4m3 [T][H][D] at offset T*H*D,
+ *   V8t e4m3 [H][D][Tp] at offset 2*T*H*D: V transposed so that keys are contiguous,
+ *     where sequence i occupies columns [pad_start(i), pad_start(i) + S_i) with
+ *     pad_start(i) = roundup(cu[i], 128) + 256*i, and every other column is 0;
+ *     Tp = roundup(T, 128) + 256*num_seqs.
+ * Returns 0 for negative or overflowing arguments.
+ */
+size_t fp8attn_workspace_bytes(int64_t total_tokens, int num_seqs, int num_heads,
+                               int head_dim);
+
+/*
+ * Quantise Q, K, V into the workspace layout above with the state's inv_scale
+ * (q8 = E4M3(fp32(x * inv_scale[t])), round to nearest even, saturating to +-448; the
+ * sign of zero is kept). This is the first half of the FP8 path of fp8attn_forward,
+ * exposed so that the bytes can be checked. cu_seqlens and cu_seqlens_host describe the
+ * same int32[num_seqs + 1] array (device and host copies).
+ * Errors: as fp8attn_forward.
+ */
+int fp8attn_quantize(const void* state, const void* q, const void* k, const void* v,
+                     const int32_t* cu_seqlens, const int32_t* cu_seqlens_host, int num_seqs,
+                     int num_heads, int head_dim, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+/*
+ * Variable-length, non-causal attention forward over packed sequences (vLLM-Omni
+ * "Quantized KV Cache", "Overview" and "Parameters"; vLLM docs "FP8 ViT Encoder
+ * Attention", "Usage"). For every sequence i, head h and query row r of that sequence:
+ *   O[r,h,:] = sum_j w_j V[j,h,:] over the keys j of sequence i only.
+ * FP8 path (flags without FP8ATTN_SKIP): quantises Q, K, V with the state's scales into
+ *   `workspace` (see fp8attn_workspace_bytes), then s_j = (q8.k8_j) * scale_q * scale_k *
+ *   softmax_scale; with m the running row maximum, p8_j = E4M3(exp(s_j - m) * 448)
+ *   (fixed scale 448, so p8_j <= 448); w_j = p8_j / sum_j p8_j; the PV product uses the
+ *   E4M3 V and is multiplied by scale_v. Accumulation and softmax are fp32; O is bf16.
+ *   Requires a preceding fp8attn_scales on this state (same stream).
+ * BF16 path (FP8ATTN_SKIP): w_j = softmax(q.k_j * softmax_scale) in fp32 with P rounded
+ *   to bf16 for the PV product; workspace and state are not used (may be NULL).
+ * softmax_scale <= 0 selects 1/sqrt(head_dim).
+ * cu_seqlens (device) and cu_seqlens_host (host) must hold the same values; the host
+ * copy is used for checks and launch sizes so that no device read-back is needed.
+ * Errors: EINVAL for NULL pointers, num_seqs < 1, num_heads < 1, total tokens beyond
+ * 2^31-1 elements per head row, a host cu_seqlens that does not start at 0 or decreases,
+ * a workspace smaller than fp8attn_workspace_bytes, unknown flag bits, or a NULL state on
+ * the FP8 path; EUNSUPPORTED for head_dim != 128.
+ */
+int fp8attn_forward(const void* state, const void* q, const void* k, const void* v,
+                    const int32_t* cu_seqlens, const int32_t* cu_seqlens_host, int num_seqs,
+                    int num_heads, int head_dim, float softmax_scale, unsigned flags,
+                    void* workspace, size_t workspace_bytes, void* out, void* stream);
+
+/* Message describing the last non-OK return on the calling thread ("" if none). */
+const char* fp8attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8ATTN_H */
