@@ -1,0 +1,223 @@
+"""Benchmark of the FP8 attention hot path on one MI355X.
+
+One step = one FP8 attention call on a batch already resident in HBM: observe the Q/K/V
+amax (amax kernel), update the scales (scales kernel), quantise Q/K/V to E4M3 (quantise
+kernel) and run the FP8 flash-attention kernel -- four launches, exactly the FP8 path of
+fp8attn_forward preceded by the dynamic-scale update. The BF16 skip-path kernel is timed
+on the same batch afterwards (same-hardware baseline). Workload: the kernel point (one
+sequence of 8192 tokens, 16 heads, head_dim 128, bf16 N(0,1) with x20 outlier columns).
+
+Prints ONE JSON line. value = attention FLOPs of the step (4 * S^2 * d * H) / step time,
+in TFLOP/s. Per-kernel durations come from HIP events recorded on the stream the kernels
+run on (torch's current stream), around each launch of the timed steps.
+
+--gpus N > 1 is refused: this build runs on one GPU.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+FP8_PEAK_TFLOPS = 5000.0      # MI355X dense FP8 MFMA (published)
+BF16_PEAK_TFLOPS = 2500.0     # MI355X dense BF16 MFMA (published)
+HBM_PEAK_GBS = 8000.0         # MI355X HBM3E (published)
+METRIC = "FP8 attn TFLOP/s & % FP8-MFMA peak at S=8192 d=128; quant GB/s"
+PMC_FILE = os.path.join(ROOT, "profiles", "attn_fp8_kernel_point_pmc.json")
+ATTN_SRC = os.path.join(ROOT, "fp8_dynamic_scaled_amd", "csrc", "attn_fp8.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="kernel")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle timing on the host cores")
+    ap.add_argument("--cpu-rows", type=int, default=16,
+                    help="query rows per head in the oracle's timed attention sample")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after the benchmark, run one plain device copy of this many MiB "
+                         "(reference for HBM byte counters)")
+    return ap.parse_args()
+
+
+def source_sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def cpu_baseline(w, q, k, v, cu, rows_per_head):
+    """Time the oracle (as it stands) on the host: full amax/scales/quantise of Q, K, V and
+    the FP8 attention of `rows_per_head` query rows per head over all keys; extrapolate the
+    attention to every row and report attention FLOPs per second of that estimate."""
+    import numpy as np
+    import oracle
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from parity_util import bits
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = 1
+    host = [bits(t) for t in (q, k, v)]
+    t0 = time.perf_counter()
+    amax = [oracle.amax_bf16(b) for b in host]
+    sc = [oracle.scale_pair(a) for a in oracle.AmaxRing().update(amax)]
+    codes = [oracle.quantize_bf16(b, s[1]) for b, s in zip(host, sc)]
+    t_quant = time.perf_counter() - t0
+    rng = np.random.default_rng(0)
+    toks = np.sort(rng.choice(w.total_tokens, size=rows_per_head, replace=False))
+    sm = float(np.float32(1.0 / math.sqrt(w.head_dim)))
+    t1 = time.perf_counter()
+    oracle.fp8_attention(codes[0], codes[1], codes[2], list(cu), sc[0][0], sc[1][0], sc[2][0],
+                         sm, tokens=toks, kv_block=64)
+    t_attn = time.perf_counter() - t1
+    frac = rows_per_head / w.total_tokens
+    t_full = t_quant + t_attn / frac
+    return {"value": w.flops() / t_full / 1e12, "unit": "TFLOP/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": (f"{w.name}: amax+scales+quantise of full Q/K/V ({t_quant:.1f} s) and "
+                       f"FP8 attention of {rows_per_head} query rows x {w.num_heads} heads over "
+                       f"all {w.seq_lens[0]} keys ({t_attn:.1f} s), attention extrapolated "
+                       f"to all rows (x{1 / frac:.0f}); value = workload FLOPs / that "
+                       f"estimate ({t_full:.0f} s)"),
+            "seconds_measured": t_quant + t_attn}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+                          "n_gpus_requested": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    import fp8_dynamic_scaled_amd as fa
+    from workloads import WORKLOADS, make_qkv
+
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    q, k, v = make_qkv(w, 0, dev)
+    cu = list(w.cu_seqlens)
+    cu_d = torch.tensor(cu, dtype=torch.int32, device=dev)
+    B, H, D, T = w.num_seqs, w.num_heads, w.head_dim, w.total_tokens
+    st = fa.new_state(dev)
+    ws = torch.empty(fa.workspace_bytes(T, B, H, D), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(q)
+    n = w.elements()
+    flops = w.flops()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        fa.observe_amax(st, q, k, v)
+        if ev is not None:
+            ev[1].record()
+        fa.scales(st, "dynamic")
+        if ev is not None:
+            ev[2].record()
+        fa.quantize(st, q, k, v, cu_d, cu, workspace=ws)
+        if ev is not None:
+            ev[3].record()
+        fa.attend(st, ws, cu_d, cu, H, out=out)
+        if ev is not None:
+            ev[4].record()
+
+    for _ in range(args.warmup):
+        step()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    per = {"amax": 0.0, "scales": 0.0, "quantize": 0.0, "attn_fp8": 0.0}
+    for e in evs:
+        per["amax"] += e[0].elapsed_time(e[1])
+        per["scales"] += e[1].elapsed_time(e[2])
+        per["quantize"] += e[2].elapsed_time(e[3])
+        per["attn_fp8"] += e[3].elapsed_time(e[4])
+    per = {k2: v2 / args.steps for k2, v2 in per.items()}       # ms per launch
+
+    # BF16 skip-path kernel on the same batch
+    for _ in range(args.warmup):
+        fa.forward(None, q, k, v, cu_d, cu, skip=True, out=out)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        fa.forward(None, q, k, v, cu_d, cu, skip=True, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_bf16 = e0.elapsed_time(e1) / args.steps
+
+    attn_tflops = flops / (per["attn_fp8"] * 1e-3) / 1e12
+    quant_gbs = (3 * n * 3) / (per["quantize"] * 1e-3) / 1e9
+    amax_gbs = (3 * n * 2) / (per["amax"] * 1e-3) / 1e9
+    bf16_tflops = flops / (ms_bf16 * 1e-3) / 1e12
+
+    traffic = None
+    if os.path.exists(PMC_FILE):
+        with open(PMC_FILE) as f:
+            pmc = json.load(f)
+        if pmc.get("kernel_source_sha256") == source_sha(ATTN_SRC) and pmc.get("workload") == w.name:
+            traffic = pmc.get("hbm_bytes_per_launch")
+
+    result = {
+        "metric": METRIC,
+        "value": round(flops / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3 (fp32 accumulate)",
+        "data": "synthetic (seeded bf16 N(0,1), 0.1% of hidden columns x20)",
+        "config": {"workload": f"{w.name}: {w.description}", "num_seqs": B, "seq_len": w.seq_lens[0],
+                   "num_heads": H, "head_dim": D, "causal": False, "scaling": "dynamic 16-slot ring"},
+        "roofline": {"bound": "mfma", "kernel": "attn_fp8_kernel",
+                     "achieved": round(attn_tflops, 2), "peak": FP8_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / FP8_PEAK_TFLOPS, 4),
+                     "traffic": traffic,
+                     "algorithmic_per_launch": f"{flops:.4e} FLOP (4*S^2*d*H)"},
+        "kernels_ms": {k2: round(v2, 5) for k2, v2 in per.items()},
+        "attn_fp8_tflops": round(attn_tflops, 2),
+        "attn_fp8_frac_fp8_peak": round(attn_tflops / FP8_PEAK_TFLOPS, 4),
+        "attn_bf16_ms": round(ms_bf16, 5),
+        "attn_bf16_tflops": round(bf16_tflops, 2),
+        "attn_bf16_frac_bf16_peak": round(bf16_tflops / BF16_PEAK_TFLOPS, 4),
+        "fp8_over_bf16_speedup": round(ms_bf16 / per["attn_fp8"], 3),
+        "quant_gbs": round(quant_gbs, 1),
+        "quant_frac_hbm_peak": round(quant_gbs / HBM_PEAK_GBS, 4),
+        "amax_gbs": round(amax_gbs, 1),
+        "amax_frac_hbm_peak": round(amax_gbs / HBM_PEAK_GBS, 4),
+        "quant_algorithmic_bytes": f"{3 * n * 3:.4e} (2 B read + 1 B write per element, 3 tensors)",
+        "amax_algorithmic_bytes": f"{3 * n * 2:.4e} (2 B read per element, 3 tensors)",
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, q, k, v, cu, args.cpu_rows)
+    if args.copy_calibration_mib > 0:
+        nb = args.copy_calibration_mib << 20
+        src = torch.empty(nb, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        result["copy_calibration_bytes"] = nb
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

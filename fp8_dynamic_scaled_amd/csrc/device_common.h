@@ -1,0 +1,61 @@
+// Device-side helpers shared by the gfx950 kernels of libfp8attn.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fp8attn.h"
+
+namespace fp8attn {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+
+constexpr int kHeadDim = 128;
+constexpr float kE4M3Max = 448.0f;
+// log2(448): folds the fixed P scale into the exponent of exp2.
+constexpr float kLog2E4M3Max = 8.807354922057604f;
+constexpr float kLog2e = 1.4426950408889634f;
+
+// bf16 halves of a packed dword as fp32 (exact).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two fp32 -> two E4M3 bytes (a in the lower byte) in the low half (HI = false) or the
+// high half of `old`. gfx950's converter rounds to nearest even and is OCP E4M3FN; it
+// only saturates up to 464, so callers that can exceed 448 clamp first.
+template <bool HI>
+__device__ __forceinline__ int cvt_pk_e4m3(float a, float b, int old) {
+  return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, HI);
+}
+
+__device__ __forceinline__ float clamp_e4m3(float y) {
+  return __builtin_fminf(__builtin_fmaxf(y, -kE4M3Max), kE4M3Max);
+}
+
+// D = A * B + C on FP8 E4M3 operands (32x32x64, fp32 accumulate). Both operands hold,
+// per lane, 32 bytes of the k dimension: lane l owns row/column l % 32 and k-half l / 32.
+__device__ __forceinline__ v16f mfma_e4m3_32x32x64(v8i a, v8i b, v16f c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// D = A * B + C on bf16 operands (32x32x16, fp32 accumulate); 8 k-values per lane.
+__device__ __forceinline__ v16f mfma_bf16_32x32x16(v8bf a, v8bf b, v16f c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ bool wave_any(bool p) {
+  return __builtin_amdgcn_ballot_w64(p) != 0;
+}
+
+// Start column of sequence i in the key-contiguous V8t layout (see fp8attn.h).
+__device__ __host__ __forceinline__ int64_t pad_start(int64_t cu_i, int i) {
+  return ((cu_i + 127) / 128) * 128 + 256 * (int64_t)i;
+}
+
+}  // namespace fp8attn

@@ -64,6 +64,9 @@ typedef enum fp8attn_status {
 #define FP8ATTN_SKIP 1u /* run the BF16 kernel on the unquantised inputs; state is not read */
 
 #define FP8ATTN_RING_SLOTS 16
+/* Keys per online-softmax block of the FP8 path: P is quantised to E4M3 relative to the
+ * running row maximum of the blocks of 64 keys seen so far (sequence order). */
+#define FP8ATTN_KV_BLOCK 64
 #define FP8ATTN_E4M3_MAX 448.0f
 #define FP8ATTN_DEFAULT_MARGIN 1.5f
 
@@ -88,7 +91,7 @@ typedef struct fp8attn_state {
   float scale[3];
   float inv_scale[3];
   float amax[3];
-  uint32_t reserved[4];
+  uint32_t reserved[3];
 } fp8attn_state;
 
 /* Size in bytes of fp8attn_state (256). */
@@ -157,15 +160,29 @@ int fp8attn_quantize(const void* state, const void* q, const void* k, const void
                      void* stream);
 
 /*
+ * FP8 attention on a workspace already filled by fp8attn_quantize with this state's
+ * scales (the second half of the FP8 path of fp8attn_forward, which is exactly
+ * fp8attn_quantize followed by fp8attn_attend). Arguments and the computation are those of
+ * fp8attn_forward's FP8 path; q, k and v are not read. Lets a caller reuse one quantised
+ * workspace, or time the attention kernel on its own.
+ * Errors: as fp8attn_forward (q, k, v are not needed and may be NULL).
+ */
+int fp8attn_attend(const void* state, const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+                   int num_seqs, int num_heads, int head_dim, float softmax_scale,
+                   const void* workspace, size_t workspace_bytes, void* out, void* stream);
+
+/*
  * Variable-length, non-causal attention forward over packed sequences (vLLM-Omni
  * "Quantized KV Cache", "Overview" and "Parameters"; vLLM docs "FP8 ViT Encoder
  * Attention", "Usage"). For every sequence i, head h and query row r of that sequence:
  *   O[r,h,:] = sum_j w_j V[j,h,:] over the keys j of sequence i only.
  * FP8 path (flags without FP8ATTN_SKIP): quantises Q, K, V with the state's scales into
  *   `workspace` (see fp8attn_workspace_bytes), then s_j = (q8.k8_j) * scale_q * scale_k *
- *   softmax_scale; with m the running row maximum, p8_j = E4M3(exp(s_j - m) * 448)
- *   (fixed scale 448, so p8_j <= 448); w_j = p8_j / sum_j p8_j; the PV product uses the
- *   E4M3 V and is multiplied by scale_v. Accumulation and softmax are fp32; O is bf16.
+ *   softmax_scale, and an online softmax over blocks of FP8ATTN_KV_BLOCK keys: with m the
+ *   running row maximum after the current block, p8_j = E4M3(exp(s_j - m) * 448) (fixed
+ *   scale 448, so p8_j <= 448); earlier sums are rescaled by exp(m_old - m) when m grows;
+ *   O = scale_v * sum_j p8'_j v8_j / sum_j p8'_j with p8' the rescaled weights. The PV
+ *   product uses the E4M3 V; accumulation and softmax are fp32; O is bf16.
  *   Requires a preceding fp8attn_scales on this state (same stream).
  * BF16 path (FP8ATTN_SKIP): w_j = softmax(q.k_j * softmax_scale) in fp32 with P rounded
  *   to bf16 for the PV product; workspace and state are not used (may be NULL).

@@ -22,7 +22,7 @@ a value ("parity unpinned" for that one quantity; it is pinned through invariant
 from .e4m3 import (E4M3_MAX, e4m3_decode, e4m3_encode, e4m3_decode_table,
                    e4m3_finite_values)
 from .numerics import bf16_bits_to_f64, f64_to_bf16_bits, round_f32
-from .scaling import (AmaxRing, RING_SLOTS, SCALE_FLOOR, amax_bf16, scale_pair,
+from .scaling import (AmaxRing, RING_SLOTS, SCALE_FLOOR, amax_bf16, amax_bf16_bits, scale_pair,
                       static_amax)
 from .quant import quantize_bf16
 from .attention import (attention_f64, fp8_attention, fp8_attention_head,
@@ -31,7 +31,8 @@ from .attention import (attention_f64, fp8_attention, fp8_attention_head,
 __all__ = [
     "E4M3_MAX", "e4m3_decode", "e4m3_encode", "e4m3_decode_table", "e4m3_finite_values",
     "bf16_bits_to_f64", "f64_to_bf16_bits", "round_f32",
-    "AmaxRing", "RING_SLOTS", "SCALE_FLOOR", "amax_bf16", "scale_pair", "static_amax",
+    "AmaxRing", "RING_SLOTS", "SCALE_FLOOR", "amax_bf16", "amax_bf16_bits", "scale_pair",
+    "static_amax",
     "quantize_bf16",
     "attention_f64", "fp8_attention", "fp8_attention_head", "bf16_reference_attention",
     "varlen_rows",

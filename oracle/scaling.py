@@ -36,6 +36,17 @@ def amax_bf16(bits):
     return float(np.max(np.abs(x)))
 
 
+def amax_bf16_bits(bits):
+    """Same value as amax_bf16, computed on the bit patterns: for finite bf16 values the
+    pattern with the sign bit cleared orders exactly like |x|, so max|x| is the value of
+    the largest such pattern. Used for large tensors (no float64 copy)."""
+    b = np.asarray(bits, dtype=np.uint16).reshape(-1)
+    if b.size == 0:
+        return 0.0
+    m = np.uint32(np.max(b & np.uint16(0x7FFF)))
+    return float(np.array([m << np.uint32(16)], dtype=np.uint32).view(np.float32)[0])
+
+
 def scale_pair(amax):
     """(scale, inv) for one tensor from its window/static amax A (a binary32 value).
 

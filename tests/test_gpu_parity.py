@@ -1,0 +1,321 @@
+"""GPU parity: the HIP path through the C-ABI against the CPU oracle.
+
+Bit-exact: amax, ring state, scales and every E4M3 byte (Q8, K8 and the key-contiguous
+V8t, including its zero padding). Attention: element by element on all rows at sizes that
+span several tiles with ragged tails, empty and single-token sequences; tolerances
+max-abs 1.5e-2 and mean-abs 2e-3 against the oracle.
+"""
+import ctypes
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import fp8_dynamic_scaled_amd as fa
+from fp8_dynamic_scaled_amd import _lib
+from workloads import draw_tensor, random_varlen
+
+from parity_util import (MAX_ABS_TOL, MEAN_ABS_TOL, bits, bf16_to_f64, check_rows, compare,
+                         cosine, hw_bound_rows, oracle_fp8_rows, oracle_ref_rows, quant_lut,
+                         v_channel_std)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+SM = fa.default_softmax_scale()
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def _cu_dev(cu):
+    return torch.tensor(cu, dtype=torch.int32, device=DEV)
+
+
+def _oracle_scales_dynamic(history):
+    """Oracle ring over a list of (q, k, v) amax triples; returns scales of the last."""
+    ring = oracle.AmaxRing()
+    A = None
+    for a in history:
+        A = ring.update(a)
+    return [oracle.scale_pair(x) for x in A], ring
+
+
+def _amax3(q, k, v):
+    return [oracle.amax_bf16(bits(t)) for t in (q, k, v)]
+
+
+# --------------------------------------------------------------------------- amax/scales
+def test_state_reset_and_dynamic_ring_bit_exact():
+    say("ring: 20 dynamic forwards, varied magnitudes")
+    st = fa.new_state(DEV)
+    s0 = fa.read_state(st)
+    assert all(np.all(v == 0) for v in s0.values())
+    history = []
+    for f in range(20):
+        g = torch.Generator(device=DEV).manual_seed(100 + f)
+        shape = (257, 3, 128)
+        q = (torch.randn(shape, device=DEV, generator=g) * (1 + f % 5)).to(torch.bfloat16)
+        k = (torch.randn(shape, device=DEV, generator=g) * (20 - f)).to(torch.bfloat16)
+        v = (torch.randn(shape, device=DEV, generator=g) * 0.01).to(torch.bfloat16)
+        fa.observe_amax(st, q, k, v)
+        fa.scales(st, "dynamic")
+        history.append(_amax3(q, k, v))
+        sc, ring = _oracle_scales_dynamic(history)
+        s = fa.read_state(st)
+        assert int(s["count"]) == f + 1
+        assert np.array_equal(s["ring"].astype(np.float64), ring.slots)
+        assert np.all(s["cur"] == 0)
+        for t in range(3):
+            assert float(s["scale"][t]) == sc[t][0], (f, t)
+            assert float(s["inv_scale"][t]) == sc[t][1], (f, t)
+
+
+def test_amax_tail_and_empty_through_c_abi():
+    say("amax: odd element counts through the raw C-ABI, n = 0")
+    lib = _lib.load()
+    st = fa.new_state(DEV)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    for n in (1, 7, 1001, 4099, 70001):
+        x = [(torch.randn(n + 8, device=DEV) * (t + 1)).to(torch.bfloat16) for t in range(3)]
+        x[1][n - 1] = -1000.0                        # the max sits in the scalar tail
+        ptrs = [ctypes.c_void_p(t.data_ptr()) for t in x]
+        _lib.check("observe", lib.fp8attn_observe_amax(ctypes.c_void_p(st.data_ptr()), *ptrs, n, stream))
+        fa.scales(st, "static", [1.0, 1.0, 1.0], 1.0)   # clears cur without touching the ring
+        # observe again and read cur directly (before scales clears it)
+        _lib.check("observe", lib.fp8attn_observe_amax(ctypes.c_void_p(st.data_ptr()), *ptrs, n, stream))
+        s = fa.read_state(st)
+        for t in range(3):
+            want = oracle.amax_bf16(bits(x[t][:n]))
+            got = float(np.array([s["cur"][t]], dtype=np.uint32).view(np.float32)[0])
+            assert got == want, (n, t)
+        fa.scales(st, "static", [1.0, 1.0, 1.0], 1.0)
+    # n = 0 observes nothing: the dynamic scale then sees an all-zero window
+    st2 = fa.new_state(DEV)
+    _lib.check("observe", lib.fp8attn_observe_amax(ctypes.c_void_p(st2.data_ptr()), None, None, None, 0, stream))
+    fa.scales(st2, "dynamic")
+    s = fa.read_state(st2)
+    want = oracle.scale_pair(0.0)
+    assert float(s["scale"][0]) == want[0] and float(s["inv_scale"][0]) == want[1]
+
+
+def test_static_scales_many_values_bit_exact():
+    say("static scales: 3000 amax values x 3 margins")
+    st = fa.new_state(DEV)
+    rng = np.random.default_rng(0)
+    pats = np.concatenate([[0, 1, 0x0080, 0x7F7F, 0x3F80, 0x4360],
+                           rng.integers(0, 0x7F80, size=3000)]).astype(np.uint16)
+    vals = oracle.bf16_bits_to_f64(pats)
+    for margin in (1.5, 1.0, 0.37):
+        for i in range(0, len(vals), 3):
+            trio = [float(x) for x in vals[i:i + 3]]
+            if len(trio) < 3:
+                break
+            fa.scales(st, "static", trio, margin)
+            s = fa.read_state(st)
+            A = oracle.static_amax(trio, margin)
+            for t in range(3):
+                sc, inv = oracle.scale_pair(A[t])
+                assert float(s["amax"][t]) == A[t]
+                assert float(s["scale"][t]) == sc and float(s["inv_scale"][t]) == inv
+            assert int(s["count"]) == 0
+
+
+# --------------------------------------------------------------------------- quantise
+def _check_workspace(ws, q, k, v, cu, sc):
+    T, H, D = q.shape
+    B = len(cu) - 1
+    q8, k8, v8t = [t.to("cpu").numpy() for t in fa.split_workspace(ws, T, B, H, D)]
+    luts = [quant_lut(s[1]) for s in sc]
+    assert np.array_equal(q8, luts[0][bits(q)])
+    assert np.array_equal(k8, luts[1][bits(k)])
+    want_v = luts[2][bits(v)]                       # [T, H, D]
+    Tp = v8t.shape[2]
+    covered = np.zeros(Tp, dtype=bool)
+    for i in range(B):
+        lo, hi = cu[i], cu[i + 1]
+        ps = fa.pad_start(lo, i)
+        assert np.array_equal(v8t[:, :, ps:ps + hi - lo], want_v[lo:hi].transpose(1, 2, 0))
+        covered[ps:ps + hi - lo] = True
+    assert np.all(v8t[:, :, ~covered] == 0)        # padding columns are zero
+
+
+@pytest.mark.parametrize("lens,H", [([1, 127, 128, 129, 300, 0, 64], 3), ([256], 2),
+                                    ([5, 0, 0, 1000], 1), ([0, 77], 4)])
+def test_quantize_bytes_bit_exact_dynamic(lens, H):
+    say(f"quantise dynamic lens={lens} H={H}")
+    q, k, v, cu = random_varlen(lens, H, seed=sum(lens) + H, device=DEV, outliers=True)
+    st = fa.new_state(DEV)
+    fa.observe_amax(st, q, k, v)
+    fa.scales(st, "dynamic")
+    sc = [oracle.scale_pair(a) for a in _amax3(q, k, v)]
+    ws = fa.quantize(st, q, k, v, _cu_dev(cu), cu)
+    torch.cuda.synchronize()
+    _check_workspace(ws, q, k, v, cu, sc)
+
+
+def test_quantize_saturates_static():
+    say("quantise static margin 0.5 (saturation)")
+    q, k, v, cu = random_varlen([300, 45], 2, seed=9, device=DEV, scale=3.0)
+    am = _amax3(q, k, v)
+    st = fa.new_state(DEV)
+    fa.scales(st, "static", am, 0.5)
+    A = oracle.static_amax(am, 0.5)
+    sc = [oracle.scale_pair(a) for a in A]
+    ws = fa.quantize(st, q, k, v, _cu_dev(cu), cu)
+    torch.cuda.synchronize()
+    _check_workspace(ws, q, k, v, cu, sc)
+    q8 = fa.split_workspace(ws, q.shape[0], 2, 2)[0].to("cpu").numpy()
+    assert np.sum((q8 & 0x7F) == 0x7E) > 10
+
+
+@pytest.mark.parametrize("amax", [1.0, 448.0, 3.0e38, 1e-20, 0.0, 2.5e-6])
+def test_quantize_every_bf16_pattern(amax):
+    say(f"quantise all finite bf16 patterns, static amax={amax}")
+    pats = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    pats = pats[(pats & 0x7F80) != 0x7F80]            # finite only (non-finite: outside contract)
+    n = (len(pats) + 127) // 128 * 128
+    buf = np.zeros(n, dtype=np.uint16)
+    buf[:len(pats)] = pats
+    x = torch.from_numpy(buf.view(np.int16)).view(torch.bfloat16).to(DEV).view(n // 128, 1, 128)
+    cu = [0, n // 128]
+    st = fa.new_state(DEV)
+    fa.scales(st, "static", [amax, amax, amax], 1.0)
+    sc = [oracle.scale_pair(oracle.static_amax([amax], 1.0)[0])] * 3
+    ws = fa.quantize(st, x, x, x, _cu_dev(cu), cu)
+    torch.cuda.synchronize()
+    _check_workspace(ws, x, x, x, cu, sc)
+
+
+# --------------------------------------------------------------------------- attention
+def _run_fp8(q, k, v, cu, static=None, margin=1.5):
+    layer = fa.AttentionLayer(DEV, static_amax=static, margin=margin)
+    out = layer(q, k, v, _cu_dev(cu), cu)
+    torch.cuda.synchronize()
+    return out, layer
+
+
+def _assert_close(tag, got, want, max_tol=MAX_ABS_TOL, mean_tol=MEAN_ABS_TOL):
+    mx, mn = compare(got, want)
+    say(f"  {tag}: max-abs {mx:.3e} mean-abs {mn:.3e}")
+    assert mx <= max_tol and mn <= mean_tol, (tag, mx, mn)
+
+
+@pytest.mark.parametrize("lens,H,outliers", [([300, 1, 77, 513, 0, 128, 64], 2, False),
+                                             ([1000], 3, True), ([63, 65, 129, 191], 2, False),
+                                             ([1], 1, False), ([2049, 31], 2, True)])
+def test_fp8_attention_all_rows(lens, H, outliers):
+    say(f"fp8 attention lens={lens} H={H} outliers={outliers}")
+    q, k, v, cu = random_varlen(lens, H, seed=len(lens) * 31 + H, device=DEV, outliers=outliers)
+    out, _ = _run_fp8(q, k, v, cu)
+    sc = [oracle.scale_pair(a) for a in _amax3(q, k, v)]
+    want = oracle_fp8_rows(q, k, v, cu, sc, SM)
+    got = bf16_to_f64(out)
+    if not outliers:
+        # unit-variance inputs: the stated tolerance, nothing else
+        _assert_close("fp8 vs oracle (online rule)", got, want)
+    else:
+        # per-channel scaled inputs: unit-variance units, plus the FP8 matrix-core bound
+        luts = [quant_lut(x[1]) for x in sc]
+        toks = np.arange(q.shape[0])
+        bound = hw_bound_rows(luts[0][bits(q)], luts[1][bits(k)], luts[2][bits(v)], cu, sc, SM, toks)
+        st = check_rows(got, want, bound, v_channel_std(v)[None])
+        say(f"  fp8 vs oracle (unit-variance units): {st}")
+        assert st["ok"], st
+    mx_g, mn_g = compare(got, oracle_fp8_rows(q, k, v, cu, sc, SM, kv_block=None))
+    say(f"  (global-max reading: max-abs {mx_g:.3e} mean-abs {mn_g:.3e})")
+    ref = oracle_ref_rows(q, k, v, cu, SM)
+    c_gpu, c_or = cosine(got, ref), cosine(want, ref)
+    say(f"  cosine vs unquantised: gpu {c_gpu:.6f} oracle {c_or:.6f}")
+    assert c_gpu >= c_or - 5e-4
+
+
+@pytest.mark.parametrize("lens,H", [([300, 1, 77, 513, 0, 128, 64], 2), ([1000], 3),
+                                    ([2049, 31], 2)])
+def test_bf16_attention_all_rows(lens, H):
+    say(f"bf16 attention lens={lens} H={H}")
+    q, k, v, cu = random_varlen(lens, H, seed=len(lens) * 17 + H, device=DEV)
+    st = fa.new_state(DEV)
+    before = st.clone()
+    out = fa.forward(st, q, k, v, _cu_dev(cu), cu, skip=True)
+    torch.cuda.synchronize()
+    assert torch.equal(st, before)                  # the skip path leaves the state alone
+    got = bf16_to_f64(out)
+    want = oracle_ref_rows(q, k, v, cu, SM)
+    _assert_close("bf16 vs oracle", got, want)
+    say(f"  cosine {cosine(got, want):.6f}")
+    assert cosine(got, want) >= 0.9999
+
+
+def test_fp8_closed_forms():
+    say("fp8 closed forms: zero query -> mean of V, constant V -> V")
+    lens, H = [200, 37], 2
+    q, k, v, cu = random_varlen(lens, H, seed=5, device=DEV)
+    qz = torch.zeros_like(q)
+    out, layer = _run_fp8(qz, k, v, cu)
+    s = fa.read_state(layer.state)
+    sv, inv_v = float(s["scale"][2]), float(s["inv_scale"][2])
+    v8 = quant_lut(inv_v)[bits(v)]
+    got = bf16_to_f64(out)
+    for i in range(len(lens)):
+        lo, hi = cu[i], cu[i + 1]
+        mean = oracle.e4m3_decode(v8[lo:hi]).mean(axis=0) * sv       # [H, D]
+        want = np.broadcast_to(mean, (hi - lo,) + mean.shape)
+        assert np.max(np.abs(got[lo:hi] - want)) <= 2.0 ** -8 * np.max(np.abs(want)) + 1e-6
+    # constant V (per head/channel): every output row equals that constant (bf16 rounding)
+    vc = v[:1].expand_as(v).contiguous()
+    out2, layer2 = _run_fp8(q, k, vc, cu)
+    s2 = fa.read_state(layer2.state)
+    v8c = quant_lut(float(s2["inv_scale"][2]))[bits(vc[:1])]
+    want = oracle.e4m3_decode(v8c[0]) * float(s2["scale"][2])
+    got = bf16_to_f64(out2)
+    assert np.max(np.abs(got - want[None])) <= 2.0 ** -8 * np.max(np.abs(want)) + 1e-6
+
+
+def test_packed_equals_separate_calls():
+    say("block-diagonal isolation: packed vs per-sequence calls (static scales)")
+    lens, H = [130, 0, 257, 64, 1], 2
+    q, k, v, cu = random_varlen(lens, H, seed=77, device=DEV)
+    am = _amax3(q, k, v)
+    out, _ = _run_fp8(q, k, v, cu, static=am)
+    for i in range(len(lens)):
+        lo, hi = cu[i], cu[i + 1]
+        if hi == lo:
+            continue
+        sub = [t[lo:hi].contiguous() for t in (q, k, v)]
+        o_i, _ = _run_fp8(*sub, [0, hi - lo], static=am)
+        assert torch.equal(o_i, out[lo:hi]), i
+    # a perturbation of one sequence's keys leaves the others bit-identical
+    k2 = k.clone()
+    k2[cu[2]:cu[3]] = -k2[cu[2]:cu[3]]
+    out2, _ = _run_fp8(q, k2, v, cu, static=am)
+    assert torch.equal(out2[:cu[2]], out[:cu[2]]) and torch.equal(out2[cu[3]:], out[cu[3]:])
+    assert not torch.equal(out2[cu[2]:cu[3]], out[cu[2]:cu[3]])
+
+
+def test_repeated_calls_are_deterministic():
+    say("determinism: same inputs twice give identical bytes")
+    q, k, v, cu = random_varlen([700, 300], 2, seed=3, device=DEV)
+    am = _amax3(q, k, v)
+    o1, _ = _run_fp8(q, k, v, cu, static=am)
+    o2, _ = _run_fp8(q, k, v, cu, static=am)
+    assert torch.equal(o1, o2)
+    b1 = fa.forward(None, q, k, v, _cu_dev(cu), cu, skip=True)
+    b2 = fa.forward(None, q, k, v, _cu_dev(cu), cu, skip=True)
+    assert torch.equal(b1, b2)
+
+
+def test_attend_after_quantize_equals_forward():
+    say("attend(quantize(x)) == forward(x), bit for bit")
+    q, k, v, cu = random_varlen([500, 77], 2, seed=21, device=DEV)
+    st = fa.new_state(DEV)
+    fa.observe_amax(st, q, k, v)
+    fa.scales(st, "dynamic")
+    cu_d = _cu_dev(cu)
+    ws = fa.quantize(st, q, k, v, cu_d, cu)
+    o1 = fa.attend(st, ws, cu_d, cu, num_heads=2)
+    o2 = fa.forward(st, q, k, v, cu_d, cu)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)

@@ -185,3 +185,100 @@ def test_fp8_close_to_unquantised():
     ref = oracle.attention_f64(vals[0], vals[1], vals[2], sigma)
     cos = np.sum(o8 * ref) / math.sqrt(np.sum(o8 * o8) * np.sum(ref * ref))
     assert 0.998 <= cos < 0.9995
+
+
+# ---------------------------------------------------------------- online-softmax rule
+def test_online_single_block_equals_global():
+    rng = np.random.default_rng(10)
+    q8, k8, v8 = _codes(rng, (20, D), 2.0), _codes(rng, (50, D), 2.0), _codes(rng, (50, D))
+    args = (0.02, 0.03, 0.004, 1 / math.sqrt(D))
+    g = oracle.fp8_attention_head(q8, k8, v8, *args)
+    for blk in (50, 64, 1000):
+        assert np.array_equal(oracle.fp8_attention_head(q8, k8, v8, *args, kv_block=blk), g)
+
+
+def test_online_equals_global_when_first_block_holds_max():
+    rng = np.random.default_rng(11)
+    q8, k8, v8 = _codes(rng, (1, D), 2.0), _codes(rng, (300, D), 2.0), _codes(rng, (300, D))
+    raw = e4m3_decode(q8) @ e4m3_decode(k8).T
+    first = int(np.argmax(raw[0]))
+    perm = np.concatenate([[first], np.delete(np.arange(300), first)])
+    k8, v8 = k8[perm], v8[perm]
+    args = (0.02, 0.03, 0.004, 1 / math.sqrt(D))
+    g = oracle.fp8_attention_head(q8, k8, v8, *args)
+    for blk in (1, 7, 64):
+        assert np.array_equal(oracle.fp8_attention_head(q8, k8, v8, *args, kv_block=blk), g)
+
+
+def test_online_two_key_closed_form():
+    # key 1 first with score s, key 2 next with s + ln 3, blocks of one key:
+    # block 1: m = s, p8 = 448; block 2: rescale by 1/3, p8 = 448 ->
+    # O = (448/3 v1 + 448 v2) / (448/3 + 448) = (v1 + 3 v2) / 4   (global rule: 0.27027)
+    q8 = np.zeros((1, D), np.uint8)
+    k8 = np.zeros((2, D), np.uint8)
+    q8[0, 0] = e4m3_encode(np.array([2.0]))[0]
+    k8[0, 0] = e4m3_encode(np.array([2.0]))[0]
+    k8[1, 0] = e4m3_encode(np.array([4.0]))[0]
+    v8 = np.zeros((2, D), np.uint8)
+    v8[0, :] = e4m3_encode(np.array([1.0]))[0]
+    v8[1, :] = e4m3_encode(np.array([-2.0]))[0]
+    sigma = math.log(3.0) / 4.0
+    out, w, L = oracle.fp8_attention_head(q8, k8, v8, 1.0, 1.0, 1.0, sigma, return_weights=True,
+                                          kv_block=1)
+    assert np.allclose(out[0], (1.0 + 3 * -2.0) / 4.0, rtol=1e-14)
+    assert np.allclose(w[0], [0.25, 0.75], rtol=1e-14) and np.isclose(L[0], 448.0 * 4 / 3)
+    out2 = oracle.fp8_attention_head(q8, k8, v8, 1.0, 1.0, 1.0, sigma, kv_block=2)
+    assert np.allclose(out2[0], (448.0 * -2.0 + 144.0 * 1.0) / 592.0, rtol=1e-14)
+
+
+def test_online_weights_sum_to_one_and_constant_v():
+    rng = np.random.default_rng(12)
+    q8, k8 = _codes(rng, (16, D), 3.0), _codes(rng, (333, D), 3.0)
+    v8 = _codes(rng, (333, D))
+    _, w, _ = oracle.fp8_attention_head(q8, k8, v8, 0.02, 0.03, 0.004, 1 / math.sqrt(D),
+                                        return_weights=True, kv_block=64)
+    assert np.allclose(w.sum(axis=1), 1.0, rtol=0, atol=1e-13)
+    vc = np.tile(v8[:1], (333, 1))
+    out = oracle.fp8_attention_head(q8, k8, vc, 0.02, 0.03, 0.004, 1 / math.sqrt(D), kv_block=64)
+    assert np.allclose(out, e4m3_decode(v8[:1]) * 0.004, rtol=1e-13, atol=0)
+
+
+def _brute_force_online(q8, k8, v8, cu, sq, sk, sv, sigma, block):
+    """Pure-Python loops: per row, blocks of keys of its own sequence, running maximum."""
+    T, H, d = q8.shape
+    dq, dk, dv = e4m3_decode(q8), e4m3_decode(k8), e4m3_decode(v8)
+    out = np.zeros((T, H, d))
+    for i in range(len(cu) - 1):
+        lo, hi = cu[i], cu[i + 1]
+        for h in range(H):
+            for r in range(lo, hi):
+                m, L = -math.inf, 0.0
+                acc = [0.0] * d
+                for j0 in range(lo, hi, block):
+                    js = list(range(j0, min(hi, j0 + block)))
+                    sc = [sum(dq[r, h, c] * dk[j, h, c] for c in range(d)) * sq * sk * sigma
+                          for j in js]
+                    m_new = max([m] + sc)
+                    a = math.exp(m - m_new) if m != -math.inf else 0.0
+                    L *= a
+                    acc = [x * a for x in acc]
+                    for j, s in zip(js, sc):
+                        p = float(e4m3_decode(e4m3_encode(np.array([math.exp(s - m_new) * 448.0])))[0])
+                        L += p
+                        for c in range(d):
+                            acc[c] += p * dv[j, h, c]
+                    m = m_new
+                for c in range(d):
+                    out[r, h, c] = acc[c] * sv / L
+    return out
+
+
+def test_online_brute_force_varlen():
+    rng = np.random.default_rng(13)
+    cu = [0, 9, 9, 23, 40]
+    T, H, d = cu[-1], 2, 16
+    q8, k8, v8 = _codes(rng, (T, H, d), 2.0), _codes(rng, (T, H, d), 2.0), _codes(rng, (T, H, d))
+    args = (0.03, 0.02, 0.01, 0.3)
+    got = oracle.fp8_attention(q8, k8, v8, cu, *args, kv_block=5)
+    want = _brute_force_online(q8, k8, v8, cu, *args, block=5)
+    assert np.allclose(got, want, rtol=1e-12, atol=1e-15)

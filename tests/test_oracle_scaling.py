@@ -110,6 +110,11 @@ def test_amax_vs_integer_bits(seed):
     m = int(np.max(bits & 0x7FFF))
     assert a == float(oracle.bf16_bits_to_f64(np.array([m], dtype=np.uint16))[0])
     assert oracle.amax_bf16(np.zeros(0, np.uint16)) == 0.0
+    # the bit-pattern formulation gives the same value, including -0.0 and subnormals
+    assert oracle.amax_bf16_bits(bits) == a
+    special = np.array([0x8000, 0x0001, 0x8002, 0x0000], dtype=np.uint16)
+    assert oracle.amax_bf16_bits(special) == oracle.amax_bf16(special) == 2.0 ** -132
+    assert oracle.amax_bf16_bits(np.zeros(0, np.uint16)) == 0.0
 
 
 def test_quantize_saturates_under_static_small_margin():
