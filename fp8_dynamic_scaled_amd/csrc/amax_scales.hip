@@ -18,7 +18,7 @@ namespace fp8attn {
 namespace {
 
 constexpr int kAmaxThreads = 256;
-constexpr int kAmaxVec = 4;  // uint4 loads in flight per thread per iteration
+constexpr int kAmaxVec = 8;  // uint4 loads in flight per thread per iteration
 
 __device__ __forceinline__ us2 abs_pk(uint32_t w) {
   uint32_t m = w & 0x7fff7fffu;
@@ -78,8 +78,12 @@ __global__ __launch_bounds__(kAmaxThreads) void amax_kernel(fp8attn_state* st,
     uint32_t b = red[0];
 #pragma unroll
     for (int w = 1; w < kAmaxThreads / 64; ++w) b = red[w] > b ? red[w] : b;
-    // bf16 magnitude -> fp32 bit image, then fold into the pending observation
-    if (b != 0) atomicMax(&st->cur[t], b << 16);
+    // bf16 magnitude -> fp32 bit image, then fold into the pending observation; a plain
+    // load first filters the blocks that cannot raise it (atomics on one address
+    // serialise in L2)
+    const uint32_t img = b << 16;
+    if (img != 0 && img > __hip_atomic_load(&st->cur[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+      atomicMax(&st->cur[t], img);
   }
 }
 
@@ -126,9 +130,10 @@ hipError_t launch_amax(fp8attn_state* st, const uint16_t* q, const uint16_t* k,
                        const uint16_t* v, int64_t n, hipStream_t s) {
   if (n == 0) return hipSuccess;  // amax of an empty tensor is the cleared 0
   const int64_t nvec = n / 8;
-  // enough blocks to fill 256 CUs several times over, each with kAmaxVec loads in flight
+  // ~2 blocks per CU and tensor (grid-stride loops, kAmaxVec 16-byte loads in flight per
+  // thread): few enough that the per-block atomics stay cheap
   int64_t blocks = (nvec + (int64_t)kAmaxThreads * kAmaxVec - 1) / ((int64_t)kAmaxThreads * kAmaxVec);
-  if (blocks > 2048) blocks = 2048;
+  if (blocks > 512) blocks = 512;
   if (blocks < 1) blocks = 1;
   hipLaunchKernelGGL(amax_kernel, dim3((unsigned)blocks, 3), dim3(kAmaxThreads), 0, s, st, q,
                      k, v, n);
