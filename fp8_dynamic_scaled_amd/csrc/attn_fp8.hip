@@ -14,7 +14,7 @@
 //   * a block owns 128 queries of one (sequence, head); each of its 4 waves owns 32;
 //   * scores are produced transposed, S^T = K Q^T, so that in the accumulator layout a
 //     lane holds ONE query (column l % 32) and 16 keys per 32x32 block; the row maximum
-//     is then a per-lane reduction plus one exchange with lane l ^ 32;
+//     is a per-lane reduction plus one v_permlane32_swap with the other lane half;
 //   * the K rows of a tile are stored in LDS in a permuted order so that lane half g
 //     ends up holding the 32 consecutive keys g*32 .. g*32+31 of the 64-key tile; the
 //     packed E4M3 probabilities are then directly the B operand of O^T = V^T P^T, and the
@@ -23,16 +23,34 @@
 //   * O^T in the accumulator layout again puts one query per lane, so the online-softmax
 //     rescale is a per-lane multiply; it is skipped for the whole wave when no lane's
 //     maximum grew (exact: the factor would be 1);
-//   * the row sum of the quantised weights comes from one extra MFMA with an all-ones
-//     A operand (keeps it off the vector ALU, which the exp2 already saturates);
-//   * K and V8t tiles are double-buffered in LDS with a register prefetch of the next
-//     tile; LDS chunks are XOR-swizzled so operand reads are bank-conflict free;
+//   * the row sum of the quantised weights accumulates on the matrix core (one extra MFMA
+//     with an all-ones A operand per tile, into a running accumulator rescaled with O);
+//
+// Schedule. At d = 128 the vector ALU, not the matrix core, bounds this kernel: per score
+// it needs one FMA, one v_exp_f32 (about 2.3 FMA slots), half a v_cvt_pk_fp8_f32 (about
+// 1.7 slots) and part of a v_max3, and every MFMA issue blocks the ALU for a few cycles;
+// the matrix core needs 1/4 of a 32x32x64 MFMA slot per 64 scores. Keeping both busy
+// takes a software pipeline inside each wave plus two waves per SIMD:
+//   * iteration t runs the softmax of tile t on the vector ALU while the matrix core runs
+//     PV of tile t-1 and the scores of tile t+1; the MFMAs are spread through the VALU
+//     stream (sched_group_barrier), and the new P is pinned before the loop back edge so
+//     the compiler cannot sink its exp/convert chain past the next tile's rescale branch;
+//   * the rescale for tile t-1's maximum runs at the top of iteration t, after PV(t-2)
+//     was issued and before PV(t-1) is;
+//   * the loop is unrolled by two so the two score register sets swap roles without
+//     copies; a ragged last tile is handled (masked) only in the epilogue;
+//   * K and V8t tiles go global -> LDS with buffer loads that write LDS directly (no VGPR
+//     staging, no ds_write), in three-stage rings, issued two tiles ahead of use; one
+//     vmcnt wait (all but the newest tile's loads) and one barrier per tile; 16-byte LDS
+//     chunks are XOR-swizzled so operand reads are conflict-free;
 //   * exp(x - m) * 448 is computed as exp2(s * c - (m * c - log2 448)), c = scales *
 //     log2(e): one FMA and one v_exp_f32 per score;
 //   * block -> work mapping is XCD-aware: consecutive work units (q-tiles of one
 //     (sequence, head)) go to the same XCD so its L2 keeps that head's K/V.
 #include "device_common.h"
 #include "launch.h"
+
+#include <type_traits>
 
 namespace fp8attn {
 
@@ -43,8 +61,9 @@ constexpr int kBN = FP8ATTN_KV_BLOCK;     // keys per tile = online-softmax bloc
 constexpr int kThreads = 256;
 constexpr int kKTileBytes = kBN * kHeadDim;   // K tile: 64 rows x 128 B
 constexpr int kVTileBytes = kHeadDim * kBN;   // V8t tile: 128 rows x 64 B
-constexpr int kStageBytes = kKTileBytes + kVTileBytes;
+constexpr int kStages = 3;                    // ring depth of each of K and V8t
 constexpr uint32_t kOnesE4M3 = 0x38383838u;   // four E4M3 1.0
+constexpr int kBufferFlags = 0x00020000;      // raw buffer resource, dword 3 (gfx9)
 
 // LDS row of key kappa (0..63) in the K tile: the MFMA A row m of key block kb that
 // yields, in the accumulator layout, key g*32 + kb*16 + i in register i of lane half g.
@@ -52,8 +71,14 @@ __device__ __forceinline__ int k_lds_row(int kappa) {
   const int g = kappa >> 5, kb = (kappa >> 4) & 1, i = kappa & 15;
   return kb * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
 }
+// 16-byte chunk swizzles. K rows are 128 B (8 chunks), V8t rows 64 B (4 chunks). An MFMA
+// operand read has 8 (or 16) consecutive lanes on 8 (16) consecutive rows at the same
+// logical chunk; these XOR patterns spread them over distinct bank groups whether the LDS
+// serves 8 lanes over 128 B or 16 lanes over 256 B per pass.
+__device__ __forceinline__ int k_swz(int R) { return ((R >> 1) ^ (R << 2)) & 7; }
+__device__ __forceinline__ int v_swz(int R) { return ((R >> 1) ^ (R >> 2)) & 3; }
 
-__device__ __forceinline__ v8i lds_load32(const uint8_t* p0, const uint8_t* p1) {
+__device__ __forceinline__ v8i load32(const uint8_t* p0, const uint8_t* p1) {
   const v4i a = *reinterpret_cast<const v4i*>(p0);
   const v4i b = *reinterpret_cast<const v4i*>(p1);
   v8i r;
@@ -62,13 +87,127 @@ __device__ __forceinline__ v8i lds_load32(const uint8_t* p0, const uint8_t* p1) 
   return r;
 }
 
+// Per-lane constants of one wave (query n = lane % 32, k-half g = lane / 32).
+struct Lane {
+  int n, g;
+  int ks00, ks01, ks10, ks11;   // K operand chunk offsets (step s, half h) within a row
+  int vs0, vs1;                 // V8t operand chunk offsets (half h) within a row
+};
+
+// S^T = K Q^T for the 64 keys of one LDS K stage: two 32x32 blocks of fp32 scores.
+__device__ __forceinline__ void scores(const uint8_t* __restrict__ kt, const Lane& ln,
+                                       const v8i& qb0, const v8i& qb1, v16f& s0, v16f& s1) {
+  const v16f zero16 = {};
+  const uint8_t* r0 = kt + ln.n * kHeadDim;            // K block 0 row of this lane
+  const uint8_t* r1 = r0 + 32 * kHeadDim;              // K block 1 row
+  s0 = mfma_e4m3_32x32x64(load32(r0 + ln.ks00, r0 + ln.ks01), qb0, zero16);
+  s1 = mfma_e4m3_32x32x64(load32(r1 + ln.ks00, r1 + ln.ks01), qb0, zero16);
+  s0 = mfma_e4m3_32x32x64(load32(r0 + ln.ks10, r0 + ln.ks11), qb1, s0);
+  s1 = mfma_e4m3_32x32x64(load32(r1 + ln.ks10, r1 + ln.ks11), qb1, s1);
+}
+
+// O^T += V^T P^T over 4 blocks of 32 channels; the row sum of P accumulates in rs.
+__device__ __forceinline__ void pv(const uint8_t* __restrict__ vt, const Lane& ln, const v8i& p,
+                                   const v8i& ones, v16f& rs, v16f& o0, v16f& o1, v16f& o2,
+                                   v16f& o3) {
+  const uint8_t* vr = vt + ln.n * kBN;
+  rs = mfma_e4m3_32x32x64(ones, p, rs);
+  o0 = mfma_e4m3_32x32x64(load32(vr + ln.vs0, vr + ln.vs1), p, o0);
+  o1 = mfma_e4m3_32x32x64(load32(vr + 32 * kBN + ln.vs0, vr + 32 * kBN + ln.vs1), p, o1);
+  o2 = mfma_e4m3_32x32x64(load32(vr + 64 * kBN + ln.vs0, vr + 64 * kBN + ln.vs1), p, o2);
+  o3 = mfma_e4m3_32x32x64(load32(vr + 96 * kBN + ln.vs0, vr + 96 * kBN + ln.vs1), p, o3);
+}
+
+// Maximum over the two lane halves (lanes l and l ^ 32 hold the two key halves of one
+// query): one v_permlane32_swap exchanges the halves.
+__device__ __forceinline__ float half_swap_max(float mx) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                   false, false);
+  return __builtin_fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+
+// Scores i0 .. i0+3 of one 16-score block -> 4 packed E4M3 weights exp2(s*c - mc). The
+// low-half convert keeps the high half of its "old" operand, which the high-half convert
+// then overwrites; passing the first exp's own bits there lets the result take that
+// register in place (no zeroing move).
+__device__ __forceinline__ int quant4(const v16f& s, int i0, float c, float mc) {
+  const float e0 = fast_exp2(__builtin_fmaf(s[i0], c, -mc));
+  const int w = cvt_pk_e4m3<false>(e0, fast_exp2(__builtin_fmaf(s[i0 + 1], c, -mc)),
+                                   __float_as_int(e0));
+  return cvt_pk_e4m3<true>(fast_exp2(__builtin_fmaf(s[i0 + 2], c, -mc)),
+                           fast_exp2(__builtin_fmaf(s[i0 + 3], c, -mc)), w);
+}
+
+// Row maximum of this lane's query over one tile of scores (both lane halves). Masked
+// keys (g*32 + i, g*32 + 16 + i at or past key_lim) are left out.
+template <bool MASK>
+__device__ __forceinline__ float tile_max(const v16f& s0, const v16f& s1, int g, int key_lim) {
+  auto val = [&](const v16f& s, int i, int key) __attribute__((always_inline)) {
+    return (MASK && key >= key_lim) ? -__builtin_inff() : s[i];
+  };
+  // one running chain (the compiler folds it into v_max3 without re-quieting every input)
+  float mx = __builtin_fmaxf(val(s0, 0, g * 32), val(s0, 1, g * 32 + 1));
+#pragma unroll
+  for (int i = 2; i < 16; ++i) mx = __builtin_fmaxf(mx, val(s0, i, g * 32 + i));
+#pragma unroll
+  for (int i = 0; i < 16; ++i) mx = __builtin_fmaxf(mx, val(s1, i, g * 32 + 16 + i));
+  return half_swap_max(mx);
+}
+
+// p = exp(s - m) * 448 = exp2(s*c - mc), mc = m*c - log2 448; packed E4M3 with byte j of
+// the 32 = key g*32 + j of the tile. Masked keys get exp2(-inf) = 0 (the exponent
+// argument, not the score, is replaced, so a zero c cannot make -inf * 0).
+template <bool MASK>
+__device__ __forceinline__ v8i quantise_p(const v16f& s0, const v16f& s1, float c, float mc,
+                                          int g, int key_lim) {
+  auto arg = [&](float s, int key) __attribute__((always_inline)) {
+    const float x = __builtin_fmaf(s, c, -mc);
+    return (MASK && key >= key_lim) ? -__builtin_inff() : x;
+  };
+  v8i p;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int i0 = r * 4;
+    const int k0 = g * 32 + i0, k1 = g * 32 + 16 + i0;
+    // the low-half convert leaves the high half of its destination as it finds it; the
+    // high-half convert then overwrites it, so the starting value does not matter
+    const int any = __builtin_nondeterministic_value(0);
+    const int w = cvt_pk_e4m3<false>(fast_exp2(arg(s0[i0], k0)), fast_exp2(arg(s0[i0 + 1], k0 + 1)),
+                                     any);
+    p[r] = cvt_pk_e4m3<true>(fast_exp2(arg(s0[i0 + 2], k0 + 2)),
+                             fast_exp2(arg(s0[i0 + 3], k0 + 3)), w);
+    const int w2 = cvt_pk_e4m3<false>(fast_exp2(arg(s1[i0], k1)),
+                                      fast_exp2(arg(s1[i0 + 1], k1 + 1)), any);
+    p[4 + r] = cvt_pk_e4m3<true>(fast_exp2(arg(s1[i0 + 2], k1 + 2)),
+                                 fast_exp2(arg(s1[i0 + 3], k1 + 3)), w2);
+  }
+  return p;
+}
+
+// Wait for this thread's older LDS-bound tile loads (all but the newest N vector-memory
+// operations), then a workgroup barrier that publishes them. The barrier is an asm
+// statement with a memory clobber, so no LDS access moves across it; __syncthreads()
+// would add its release fence, i.e. a wait for ALL outstanding loads (no lookahead left).
+template <int N>
+__device__ __forceinline__ void loads_barrier() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// Keeps p's computation above this point (an empty asm that reads it).
+__device__ __forceinline__ void pin(const v8i& p) {
+  asm volatile("" ::"v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]), "v"(p[4]), "v"(p[5]),
+               "v"(p[6]), "v"(p[7]));
+}
+
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__ k8,
                      const uint8_t* __restrict__ v8t, const int32_t* __restrict__ cu,
                      int num_seqs, int H, int64_t Tp, int qtiles, int units_per_xcd,
                      const fp8attn_state* __restrict__ st, float sm_scale,
                      uint16_t* __restrict__ out) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStageBytes];
+  // kStages K tiles, then kStages V8t tiles
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * (kKTileBytes + kVTileBytes)];
 
   // ---- work unit: XCD-aware decode, q-tile fastest
   const int L = blockIdx.x;
@@ -84,182 +223,263 @@ void attn_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int n = lane & 31, g = lane >> 5;
-  const int64_t row_stride = (int64_t)H * kHeadDim;
+  Lane ln;
+  ln.n = lane & 31;
+  ln.g = lane >> 5;
+  const int row_stride = H * kHeadDim;   // bytes per token row of Q8/K8
+
+  // ---- tile loaders: buffer loads straight into LDS. A wave's load instruction fills
+  // 1 KB of LDS with lane L at byte 16 L, so each lane fetches the global chunk that
+  // belongs at its LDS position: K block b (8 rows of 128 B) row R = 8b + L/8, physical
+  // chunk L % 8 = logical chunk ^ k_swz(R), key = the key stored at row R; V8t block b
+  // (16 rows of 64 B) row R = 16b + L/4, chunk L % 4 = logical ^ v_swz(R). Each of the
+  // 4 waves loads blocks 2w and 2w + 1 of each tile.
+  const uint8_t* kbase = k8 + (int64_t)seq_begin * row_stride + head * kHeadDim;
+  const uint8_t* vbase = v8t + (int64_t)head * kHeadDim * Tp + pad_start(seq_begin, seq);
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  int kvo[2], vvo[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int b = 2 * wv + j;
+    const int R = 8 * b + (lane >> 3);
+    const int kb = R >> 5, m = R & 31;
+    const int key = ((m >> 2) & 1) * 32 + kb * 16 + (m >> 3) * 4 + (m & 3);   // inverse of k_lds_row
+    kvo[j] = key * row_stride + (((lane & 7) ^ k_swz(R)) << 4);
+    const int RV = 16 * b + (lane >> 2);
+    vvo[j] = RV * (int)Tp + (((lane & 3) ^ v_swz(RV)) << 4);
+  }
+  const int kvo0 = kvo[0], kvo1 = kvo[1], vvo0 = vvo[0], vvo1 = vvo[1];
+  typedef __attribute__((address_space(3))) void lds_void;
+  uint8_t* const kst = smem;                                // K stage i at kst + i * kKTileBytes
+  uint8_t* const vst = smem + kStages * kKTileBytes;        // V stage i at vst + i * kVTileBytes
+  const int ntiles = (S + kBN - 1) / kBN;
+  // K tile j (clamped to the last tile, so the loads past the end stay in bounds and keep
+  // the per-tile load count uniform); rows at or past the end of the sequence read as 0
+  auto load_k = [&](int j, int stage) __attribute__((always_inline)) {
+    const int k0 = (j < ntiles ? j : ntiles - 1) * kBN;
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(kbase + (int64_t)k0 * row_stride), (short)0, (S - k0) * row_stride, kBufferFlags);
+    uint8_t* dst = kst + stage * kKTileBytes + wv * 2048;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)dst, 16, kvo0, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(dst + 1024), 16, kvo1, 0, 0, 0);
+  };
+  // V8t tile j (< ntiles): columns up to the sequence's 128-aligned padded length, which
+  // the quantise kernel zero-fills
+  auto load_v = [&](int j, int stage) __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(vbase + j * kBN), (short)0, 0x7fffffff, kBufferFlags);
+    uint8_t* dst = vst + stage * kVTileBytes + wv * 2048;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)dst, 16, vvo0, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(dst + 1024), 16, vvo1, 0, 0, 0);
+  };
+
+  // ---- prologue loads: K(0), K(1), K(2), V(0) into stages 0, 1, 2, 0. From here on the
+  // newest four vector-memory operations of a thread are always the previous tile's K and
+  // V loads, so "vmcnt(4)" at the top of iteration t means K(t+1) and V(t-1) have landed.
+  load_k(0, 0);
+  load_k(1, 1);
+  load_k(2, 2);
+  load_v(0, 0);
 
   // ---- Q^T operand (B of S^T = K Q^T): lane = query n, 32 channel bytes of half g
-  const int q_local = qt * kBM + wave * 32 + n;
+  const int q_local = qt * kBM + wave * 32 + ln.n;
   const int q_row = seq_begin + (q_local < S ? q_local : S - 1);
   const uint8_t* qp = q8 + (int64_t)q_row * row_stride + head * kHeadDim;
-  v8i qb[2];
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    const v4i a = *reinterpret_cast<const v4i*>(qp + s * 64 + g * 32);
-    const v4i b = *reinterpret_cast<const v4i*>(qp + s * 64 + g * 32 + 16);
-    qb[s][0] = a[0]; qb[s][1] = a[1]; qb[s][2] = a[2]; qb[s][3] = a[3];
-    qb[s][4] = b[0]; qb[s][5] = b[1]; qb[s][6] = b[2]; qb[s][7] = b[3];
-  }
+  const v8i qb0 = load32(qp + ln.g * 32, qp + ln.g * 32 + 16);       // channels 0..63
+  const v8i qb1 = load32(qp + 64 + ln.g * 32, qp + 64 + ln.g * 32 + 16);
 
   const float scale_q = st->scale[0], scale_k = st->scale[1], scale_v = st->scale[2];
   const float c = scale_q * scale_k * sm_scale * kLog2e;  // score -> log2 domain
 
-  // ---- tile loaders: each thread moves 2 K chunks and 2 V8t chunks of 16 bytes
-  const uint8_t* kbase = k8 + (int64_t)seq_begin * row_stride + head * kHeadDim;
-  const uint8_t* vbase = v8t + (int64_t)head * kHeadDim * Tp + pad_start(seq_begin, seq);
-  const int k_key0 = tid >> 3, k_ch = tid & 7;        // keys k_key0, k_key0 + 32
-  const int v_row0 = tid >> 2, v_ch = tid & 3;        // channel rows v_row0, v_row0 + 64
-  const int kR0 = k_lds_row(k_key0), kR1 = k_lds_row(k_key0 + 32);
-  const int k_off0 = kR0 * kHeadDim + ((k_ch ^ (kR0 & 7)) << 4);
-  const int k_off1 = kR1 * kHeadDim + ((k_ch ^ (kR1 & 7)) << 4);
-  const int v_off0 = kKTileBytes + v_row0 * kBN + ((v_ch ^ ((v_row0 >> 1) & 3)) << 4);
-  const int v_off1 = kKTileBytes + (v_row0 + 64) * kBN + ((v_ch ^ (((v_row0 + 64) >> 1) & 3)) << 4);
-  const uint8_t* vsrc0 = vbase + (int64_t)v_row0 * Tp + (v_ch << 4);
-  const uint8_t* vsrc1 = vbase + (int64_t)(v_row0 + 64) * Tp + (v_ch << 4);
-  uint4 kreg0, kreg1, vreg0, vreg1;
-#define FP8ATTN_LOAD_TILE(k0_)                                                              \
-  do {                                                                                      \
-    const int ka_ = (k0_) + k_key0 < S ? (k0_) + k_key0 : S - 1;                            \
-    const int kb_ = (k0_) + k_key0 + 32 < S ? (k0_) + k_key0 + 32 : S - 1;                  \
-    kreg0 = *reinterpret_cast<const uint4*>(kbase + (int64_t)ka_ * row_stride + (k_ch << 4)); \
-    kreg1 = *reinterpret_cast<const uint4*>(kbase + (int64_t)kb_ * row_stride + (k_ch << 4)); \
-    vreg0 = *reinterpret_cast<const uint4*>(vsrc0 + (k0_));                                 \
-    vreg1 = *reinterpret_cast<const uint4*>(vsrc1 + (k0_));                                 \
-  } while (0)
-#define FP8ATTN_STORE_TILE(stage_)                                                          \
-  do {                                                                                      \
-    uint8_t* b_ = smem + (stage_) * kStageBytes;                                            \
-    *reinterpret_cast<uint4*>(b_ + k_off0) = kreg0;                                         \
-    *reinterpret_cast<uint4*>(b_ + k_off1) = kreg1;                                         \
-    *reinterpret_cast<uint4*>(b_ + v_off0) = vreg0;                                         \
-    *reinterpret_cast<uint4*>(b_ + v_off1) = vreg1;                                         \
-  } while (0)
+  // ---- lane constants of the operand reads
+  {
+    const int sk = k_swz(ln.n), sv = v_swz(ln.n);   // the same for every 32-row block
+    ln.ks00 = ((0 + ln.g * 2) ^ sk) << 4;
+    ln.ks01 = ((1 + ln.g * 2) ^ sk) << 4;
+    ln.ks10 = ((4 + ln.g * 2) ^ sk) << 4;
+    ln.ks11 = ((5 + ln.g * 2) ^ sk) << 4;
+    ln.vs0 = ((ln.g * 2) ^ sv) << 4;
+    ln.vs1 = ((ln.g * 2 + 1) ^ sv) << 4;
+  }
 
   // ---- per-lane state for query n
-  float m_run = -__builtin_inff();
-  float l_run = 0.0f;
-  v16f o[4];
-#pragma unroll
-  for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) o[cb][i] = 0.0f;
+  // m_prev: running maximum after the last tile whose softmax ran; m_ref: the maximum that
+  // the O and row-sum accumulators are relative to (they catch up at the top of each
+  // iteration, before the pending PV is issued, so the rescale never sits between the
+  // softmax and the MFMAs it overlaps).
+  float m_prev = -__builtin_inff();
+  float m_ref = -__builtin_inff();
+  v16f o0 = {}, o1 = {}, o2 = {}, o3 = {};
+  v16f rs = {};                                         // row sum of P (entry 0 is used)
   v8i ones;
 #pragma unroll
   for (int r = 0; r < 8; ++r) ones[r] = (int)kOnesE4M3;
-  const v16f zero16 = {};
+  asm volatile("" : "+v"(ones));   // opaque: kept in registers, not rebuilt every tile
+  const int last_lim = S - (ntiles - 1) * kBN;          // valid keys of the last tile
+  v16f sa0, sa1, sb0, sb1;                              // two score register sets
+  v8i p_prev;                                           // quantised P of the previous tile
 
-  // lane-invariant parts of the operand addresses
-  const int a_row = n;                                   // MFMA A row of this lane
-  const int ntiles = (S + kBN - 1) / kBN;
+  // ---- scores of tile 0. The Q loads are younger than the prologue's tile loads and are
+  // counted by vmcnt too: wait for everything once here.
+  loads_barrier<0>();
+  scores(kst, ln, qb0, qb1, sa0, sa1);
 
-  FP8ATTN_LOAD_TILE(0);
-  FP8ATTN_STORE_TILE(0);
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
-    const bool has_next = t + 1 < ntiles;
-    if (has_next) FP8ATTN_LOAD_TILE((t + 1) * kBN);
-    const uint8_t* kt = smem + (t & 1) * kStageBytes;
-    const uint8_t* vt = kt + kKTileBytes;
-
-    // S^T = K Q^T for two 32-key blocks
-    v16f sacc[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int R = kb * 32 + a_row;
-      const uint8_t* rowp = kt + R * kHeadDim;
-      v16f acc = zero16;
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const int c0 = s * 4 + g * 2;
-        const v8i a = lds_load32(rowp + ((c0 ^ (R & 7)) << 4), rowp + (((c0 + 1) ^ (R & 7)) << 4));
-        acc = mfma_e4m3_32x32x64(a, qb[s], acc);
-      }
-      sacc[kb] = acc;
+  auto catch_up = [&]() __attribute__((always_inline)) {
+    if (wave_any(m_prev > m_ref)) {
+      // 0 while m_ref = -inf; the clamp keeps a zero c from making -inf * 0
+      const float alpha = fast_exp2(__builtin_fmaxf((m_ref - m_prev) * c, -1.0e30f));
+      rs[0] *= alpha;
+      o0 *= alpha;
+      o1 *= alpha;
+      o2 *= alpha;
+      o3 *= alpha;
     }
+    m_ref = m_prev;
+  };
 
-    // mask keys beyond the sequence (last tile only)
-    const int k0 = t * kBN;
-    if (k0 + kBN > S) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (k0 + g * 32 + kb * 16 + i >= S) sacc[kb][i] = -__builtin_inff();
+  // Stage rotation: a = t % 3 (K(t) stage, where K(t+3) goes), b = (t+1) % 3 (K(t+1) to
+  // read, V(t+1) to load), cst = (t+2) % 3 = (t-1) % 3 (V(t-1) to read).
+  int sa = 0, sb = 1, sc = 2;
+  auto rotate = [&]() __attribute__((always_inline)) {
+    const int x = sa;
+    sa = sb;
+    sb = sc;
+    sc = x;
+  };
+
+  // Iteration t < ntiles - 1: softmax of tile t (scores in cur), scores of tile t+1 into
+  // nxt, PV of tile t-1 (when t > 0). The stages being loaded (K stage t%3, last read by
+  // S(t) in iteration t-1; V stage (t+1)%3, last read by PV(t-2) in iteration t-1) are
+  // free once every wave has passed the barrier.
+  auto iteration = [&](int t, v16f& cur0, v16f& cur1, v16f& nxt0, v16f& nxt1,
+                       auto do_pv) __attribute__((always_inline)) {
+    constexpr bool PV = decltype(do_pv)::value;
+    loads_barrier<4>();   // K(t+1), V(t-1) landed; only the previous tile's 4 loads pending
+    load_k(t + 3, sa);
+    load_v(t + 1, sb);
+    if (PV) catch_up();
+    // ---- one region, written in issue order: each MFMA is followed by one chunk of the
+    // softmax (a part of the row maximum, or the exp/convert of 4 scores), and
+    // sched_barrier(0) keeps every pair where it is, so the matrix core always has the
+    // next MFMA queued while the vector ALU works through the chunk.
+    const uint8_t* vr = vst + sc * kVTileBytes + ln.n * kBN;        // V(t-1) row of lane
+    const uint8_t* kr0 = kst + sb * kKTileBytes + ln.n * kHeadDim;  // K(t+1) rows of lane
+    const uint8_t* kr1 = kr0 + 32 * kHeadDim;
+    const v16f zero16 = {};
+    v8i va0, va1, va2, va3;
+    if (PV) {
+      va0 = load32(vr + ln.vs0, vr + ln.vs1);
+      va1 = load32(vr + 32 * kBN + ln.vs0, vr + 32 * kBN + ln.vs1);
+      va2 = load32(vr + 64 * kBN + ln.vs0, vr + 64 * kBN + ln.vs1);
+      va3 = load32(vr + 96 * kBN + ln.vs0, vr + 96 * kBN + ln.vs1);
     }
-
-    // running maximum of this lane's query
-    float mx = sacc[0][0];
+    __builtin_amdgcn_sched_barrier(0);
+    if (PV) rs = mfma_e4m3_32x32x64(ones, p_prev, rs);
+    float mx = __builtin_fmaxf(cur0[0], cur0[1]);
 #pragma unroll
-    for (int i = 1; i < 16; ++i) mx = __builtin_fmaxf(mx, sacc[0][i]);
+    for (int i = 2; i < 16; ++i) mx = __builtin_fmaxf(mx, cur0[i]);
+    __builtin_amdgcn_sched_barrier(0);
+    if (PV) o0 = mfma_e4m3_32x32x64(va0, p_prev, o0);
+    const v8i ka0 = load32(kr0 + ln.ks00, kr0 + ln.ks01);
+    const v8i kb0 = load32(kr1 + ln.ks00, kr1 + ln.ks01);
+    const v8i ka1 = load32(kr0 + ln.ks10, kr0 + ln.ks11);
+    const v8i kb1 = load32(kr1 + ln.ks10, kr1 + ln.ks11);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) mx = __builtin_fmaxf(mx, sacc[1][i]);
-    mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = __builtin_fmaxf(m_run, mx);
-    if (t > 0 && wave_any(m_new > m_run)) {
-      const float alpha = fast_exp2((m_run - m_new) * c);
-      l_run *= alpha;
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[cb][i] *= alpha;
-    }
-    m_run = m_new;
-
-    // p = exp(s - m) * 448 = exp2(s*c - (m*c - log2 448)), packed to E4M3
-    const float mc = m_run * c - kLog2E4M3Max;
+    for (int i = 0; i < 16; ++i) mx = __builtin_fmaxf(mx, cur1[i]);
+    const float m_cur = __builtin_fmaxf(m_prev, half_swap_max(mx));
+    const float mc = m_cur * c - kLog2E4M3Max;
+    __builtin_amdgcn_sched_barrier(0);
     v8i p;
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int kb = r >> 2, i0 = (r & 3) * 4;
-      const float e0 = fast_exp2(__builtin_fmaf(sacc[kb][i0 + 0], c, -mc));
-      const float e1 = fast_exp2(__builtin_fmaf(sacc[kb][i0 + 1], c, -mc));
-      const float e2 = fast_exp2(__builtin_fmaf(sacc[kb][i0 + 2], c, -mc));
-      const float e3 = fast_exp2(__builtin_fmaf(sacc[kb][i0 + 3], c, -mc));
-      int w = cvt_pk_e4m3<false>(e0, e1, 0);
-      p[r] = cvt_pk_e4m3<true>(e2, e3, w);
+    if (PV) o1 = mfma_e4m3_32x32x64(va1, p_prev, o1);
+    p[0] = quant4(cur0, 0, c, mc);
+    __builtin_amdgcn_sched_barrier(0);
+    if (PV) o2 = mfma_e4m3_32x32x64(va2, p_prev, o2);
+    p[1] = quant4(cur0, 4, c, mc);
+    __builtin_amdgcn_sched_barrier(0);
+    if (PV) o3 = mfma_e4m3_32x32x64(va3, p_prev, o3);
+    p[2] = quant4(cur0, 8, c, mc);
+    __builtin_amdgcn_sched_barrier(0);
+    nxt0 = mfma_e4m3_32x32x64(ka0, qb0, zero16);
+    p[3] = quant4(cur0, 12, c, mc);
+    __builtin_amdgcn_sched_barrier(0);
+    nxt1 = mfma_e4m3_32x32x64(kb0, qb0, zero16);
+    p[4] = quant4(cur1, 0, c, mc);
+    __builtin_amdgcn_sched_barrier(0);
+    nxt0 = mfma_e4m3_32x32x64(ka1, qb1, nxt0);
+    p[5] = quant4(cur1, 4, c, mc);
+    __builtin_amdgcn_sched_barrier(0);
+    nxt1 = mfma_e4m3_32x32x64(kb1, qb1, nxt1);
+    p[6] = quant4(cur1, 8, c, mc);
+    __builtin_amdgcn_sched_barrier(0);
+    p[7] = quant4(cur1, 12, c, mc);
+    pin(p);
+    p_prev = p;
+    m_prev = m_cur;
+    rotate();
+  };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+
+  // ---- main loop over t = 0 .. ntiles-2, unrolled by two (scores alternate a <-> b)
+  int t = 0;
+  if (ntiles > 1) {
+    iteration(0, sa0, sa1, sb0, sb1, F_{});
+    t = 1;
+    for (; t + 2 < ntiles; t += 2) {
+      iteration(t, sb0, sb1, sa0, sa1, T_{});
+      iteration(t + 1, sa0, sa1, sb0, sb1, T_{});
     }
-
-    // row sum of the quantised weights on the matrix core
-    const v16f rs = mfma_e4m3_32x32x64(ones, p, zero16);
-    l_run += rs[0];
-
-    // O^T += V^T P^T over 4 blocks of 32 channels
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
-      const int R = cb * 32 + a_row;
-      const uint8_t* rowp = vt + R * kBN;
-      const int sw = (R >> 1) & 3;
-      const v8i a = lds_load32(rowp + (((2 * g) ^ sw) << 4), rowp + (((2 * g + 1) ^ sw) << 4));
-      o[cb] = mfma_e4m3_32x32x64(a, p, o[cb]);
+    if (t + 1 < ntiles) {
+      iteration(t, sb0, sb1, sa0, sa1, T_{});
+      ++t;
+    } else {
+      sa0 = sb0;   // the last tile's scores are in set b: move them (once)
+      sa1 = sb1;
     }
-
-    if (has_next) FP8ATTN_STORE_TILE((t + 1) & 1);
-    __syncthreads();
   }
+  // ---- epilogue: t = ntiles - 1, scores in set a
+  loads_barrier<0>();
+  if (ntiles > 1) {
+    catch_up();
+    pv(vst + sc * kVTileBytes, ln, p_prev, ones, rs, o0, o1, o2, o3);   // PV(ntiles-2)
+  }
+  {
+    const bool ragged = last_lim != kBN;
+    const float m_cur = __builtin_fmaxf(
+        m_prev, ragged ? tile_max<true>(sa0, sa1, ln.g, last_lim) : tile_max<false>(sa0, sa1, ln.g, kBN));
+    const float mc = m_cur * c - kLog2E4M3Max;
+    p_prev = ragged ? quantise_p<true>(sa0, sa1, c, mc, ln.g, last_lim)
+                    : quantise_p<false>(sa0, sa1, c, mc, ln.g, kBN);
+    m_prev = m_cur;
+  }
+  catch_up();
+  // V(ntiles-1) is in stage (ntiles-1) % 3 = sa after the rotations above
+  pv(vst + sa * kVTileBytes, ln, p_prev, ones, rs, o0, o1, o2, o3);
 
-  // ---- epilogue: O = O * scale_v / l, bf16, one query row per lane
+  // ---- O = O * scale_v / l, bf16, one query row per lane
   if (q_local < S) {
-    const float f = scale_v / l_run;
+    const float f = scale_v / rs[0];
     uint16_t* op = out + (int64_t)(seq_begin + q_local) * row_stride + head * kHeadDim;
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    auto put = [&](const v16f& o, int cb) __attribute__((always_inline)) {
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
-        typedef float f2 __attribute__((ext_vector_type(2)));
-        typedef __bf16 b2 __attribute__((ext_vector_type(2)));
-        const f2 x0 = {o[cb][i4 * 4 + 0] * f, o[cb][i4 * 4 + 1] * f};
-        const f2 x1 = {o[cb][i4 * 4 + 2] * f, o[cb][i4 * 4 + 3] * f};
+        const f2 x0 = {o[i4 * 4 + 0] * f, o[i4 * 4 + 1] * f};
+        const f2 x1 = {o[i4 * 4 + 2] * f, o[i4 * 4 + 3] * f};
         const b2 y0 = __builtin_convertvector(x0, b2);
         const b2 y1 = __builtin_convertvector(x1, b2);
         uint2 w;
         w.x = *reinterpret_cast<const uint32_t*>(&y0);
         w.y = *reinterpret_cast<const uint32_t*>(&y1);
-        const int ch = cb * 32 + i4 * 8 + g * 4;
-        *reinterpret_cast<uint2*>(op + ch) = w;
+        *reinterpret_cast<uint2*>(op + cb * 32 + i4 * 8 + ln.g * 4) = w;
       }
+    };
+    put(o0, 0);
+    put(o1, 1);
+    put(o2, 2);
+    put(o3, 3);
   }
-#undef FP8ATTN_LOAD_TILE
-#undef FP8ATTN_STORE_TILE
 }
 
 }  // namespace

@@ -78,6 +78,14 @@ int check_varlen(const char* fn, const void* q, const void* k, const void* v,
   if (T * num_heads > ((int64_t)1 << 31) - 1)
     return fail(FP8ATTN_EINVAL, "%s: total_tokens * num_heads = %lld exceeds 2^31-1", fn,
                 (long long)(T * num_heads));
+  // the attention kernels address one sequence of one tensor, and one head's V8t rows, with
+  // 32-bit buffer offsets
+  if ((int64_t)max_len * num_heads * head_dim > ((int64_t)1 << 31) - 1)
+    return fail(FP8ATTN_EUNSUPPORTED,
+                "%s: longest sequence x num_heads x head_dim = %lld exceeds 2^31-1", fn,
+                (long long)max_len * num_heads * head_dim);
+  if ((int64_t)head_dim * padded_keys(T, num_seqs) > ((int64_t)1 << 31) - 1)
+    return fail(FP8ATTN_EUNSUPPORTED, "%s: head_dim x padded tokens exceeds 2^31-1", fn);
   out->T = T;
   out->max_seqlen = max_len;
   out->Tp = padded_keys(T, num_seqs);

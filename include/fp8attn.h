@@ -192,7 +192,8 @@ int fp8attn_attend(const void* state, const int32_t* cu_seqlens, const int32_t* 
  * Errors: EINVAL for NULL pointers, num_seqs < 1, num_heads < 1, total tokens beyond
  * 2^31-1 elements per head row, a host cu_seqlens that does not start at 0 or decreases,
  * a workspace smaller than fp8attn_workspace_bytes, unknown flag bits, or a NULL state on
- * the FP8 path; EUNSUPPORTED for head_dim != 128.
+ * the FP8 path; EUNSUPPORTED for head_dim != 128, or when the longest sequence times
+ * num_heads * head_dim, or head_dim times the padded key count, reaches 2^31.
  */
 int fp8attn_forward(const void* state, const void* q, const void* k, const void* v,
                     const int32_t* cu_seqlens, const int32_t* cu_seqlens_host, int num_seqs,

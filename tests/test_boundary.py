@@ -83,6 +83,11 @@ def _fwd(lib, **kw):
     (dict(q=ctypes.c_void_p(0x10008)), -1, "aligned"),
     (dict(sm=float("nan")), -1, "softmax_scale"),
     (dict(cu_host=_cu([0, 1 << 30, (1 << 31) - 1]), H=2), -1, "exceeds"),
+    # 32-bit offsets inside the attention kernels: one sequence of one tensor ...
+    (dict(cu_host=_cu([0, 1 << 20, (1 << 20) + 8]), H=16), -2, "longest sequence"),
+    # ... and one head's V8t rows (2^17 sequences of 128 tokens: padded keys 3 * 2^24)
+    (dict(cu_host=_cu(list(range(0, (1 << 24) + 1, 128))), num_seqs=1 << 17, H=1), -2,
+     "padded tokens"),
 ])
 def test_forward_rejects(lib, kw, code, needle):
     assert _fwd(lib, **kw) == code
