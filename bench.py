@@ -9,7 +9,12 @@ sequence of 8192 tokens, 16 heads, head_dim 128, bf16 N(0,1) with x20 outlier co
 
 Prints ONE JSON line. value = attention FLOPs of the step (4 * S^2 * d * H) / step time,
 in TFLOP/s. Per-kernel durations come from HIP events recorded on the stream the kernels
-run on (torch's current stream), around each launch of the timed steps.
+run on (torch's current stream), around each launch of the timed steps (mean and median).
+
+The quantisation rate is also measured where the inputs cannot sit in the 256 MB
+Infinity Cache: on the same batch with a 512 MB device write before every launch (the
+write evicts the cache), and on the 3-image 4K batch (3 x 32400 tokens, 16 heads, 1.2 GB
+of bf16 input), each timed over back-to-back steps of amax + scales + quantise.
 
 --gpus N > 1 is refused: this build runs on one GPU.
 """
@@ -40,8 +45,10 @@ def parse():
     ap.add_argument("--workload", default="kernel")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing on the host cores")
-    ap.add_argument("--cpu-rows", type=int, default=16,
+    ap.add_argument("--cpu-rows", type=int, default=2560,
                     help="query rows per head in the oracle's timed attention sample")
+    ap.add_argument("--no-cold-quant", action="store_true",
+                    help="skip the quantisation measurements beyond the Infinity Cache")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the benchmark, run one plain device copy of this many MiB "
                          "(reference for HBM byte counters)")
@@ -89,6 +96,77 @@ def cpu_baseline(w, q, k, v, cu, rows_per_head):
                        f"to all rows (x{1 / frac:.0f}); value = workload FLOPs / that "
                        f"estimate ({t_full:.0f} s)"),
             "seconds_measured": t_quant + t_attn}
+
+
+def cold_quant(fa, w, q, k, v, cu_d, cu, st, ws, dev, reps=10):
+    """amax + scales + quantise where the bf16 inputs are not cache-resident: (1) the
+    benchmark batch with a 512 MB device write before each step, (2) the 4K batch."""
+    import torch
+    from workloads import WORKLOADS, make_qkv
+    out = {}
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    n = w.elements()
+    tot = {"amax": 0.0, "quantize": 0.0, "step": 0.0}
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for r in range(reps + 2):
+        flush.fill_(r & 0xff)
+        ev[0].record()
+        fa.observe_amax(st, q, k, v)
+        ev[1].record()
+        fa.scales(st, "dynamic")
+        ev[2].record()
+        fa.quantize(st, q, k, v, cu_d, cu, workspace=ws)
+        ev[3].record()
+        torch.cuda.synchronize()
+        if r >= 2:
+            tot["amax"] += ev[0].elapsed_time(ev[1]) / reps
+            tot["quantize"] += ev[2].elapsed_time(ev[3]) / reps
+            tot["step"] += ev[0].elapsed_time(ev[3]) / reps
+    out[w.name + "_flushed"] = {
+        "amax_ms": round(tot["amax"], 5), "quantize_ms": round(tot["quantize"], 5),
+        "amax_scales_quantize_ms": round(tot["step"], 5),
+        "quant_gbs": round(3 * n * 3 / (tot["quantize"] * 1e-3) / 1e9, 1),
+        "amax_gbs": round(3 * n * 2 / (tot["amax"] * 1e-3) / 1e9, 1),
+        "dynamic_path_gbs": round(3 * n * 5 / (tot["step"] * 1e-3) / 1e9, 1),
+        "note": "512 MB device write before every launch; bytes: amax 2 B, quantise 3 B, "
+                "the dynamic path 5 B per element of Q, K, V"}
+    del flush
+    w4 = WORKLOADS["4k"]
+    q4, k4, v4 = make_qkv(w4, 0, dev)
+    cu4 = list(w4.cu_seqlens)
+    cu4_d = torch.tensor(cu4, dtype=torch.int32, device=dev)
+    st4 = fa.new_state(dev)
+    ws4 = torch.empty(fa.workspace_bytes(w4.total_tokens, w4.num_seqs, w4.num_heads,
+                                         w4.head_dim), dtype=torch.uint8, device=dev)
+    n4 = w4.elements()
+    for _ in range(2):
+        fa.observe_amax(st4, q4, k4, v4)
+        fa.scales(st4, "dynamic")
+        fa.quantize(st4, q4, k4, v4, cu4_d, cu4, workspace=ws4)
+    e = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(reps)]
+    torch.cuda.synchronize()
+    for r in range(reps):
+        e[r][0].record()
+        fa.observe_amax(st4, q4, k4, v4)
+        e[r][1].record()
+        fa.scales(st4, "dynamic")
+        e[r][2].record()
+        fa.quantize(st4, q4, k4, v4, cu4_d, cu4, workspace=ws4)
+        e[r][3].record()
+    torch.cuda.synchronize()
+    am = sum(x[0].elapsed_time(x[1]) for x in e) / reps
+    qm = sum(x[2].elapsed_time(x[3]) for x in e) / reps
+    sm = sum(x[0].elapsed_time(x[3]) for x in e) / reps
+    out["4k"] = {
+        "elements_per_tensor": n4, "amax_ms": round(am, 5), "quantize_ms": round(qm, 5),
+        "amax_scales_quantize_ms": round(sm, 5),
+        "quant_gbs": round(3 * n4 * 3 / (qm * 1e-3) / 1e9, 1),
+        "amax_gbs": round(3 * n4 * 2 / (am * 1e-3) / 1e9, 1),
+        "dynamic_path_gbs": round(3 * n4 * 5 / (sm * 1e-3) / 1e9, 1),
+        "note": "3 x 32400 tokens, 16 heads: 1.19 GB bf16 in, 0.6 GB E4M3 out per step"}
+    del q4, k4, v4, ws4
+    torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -141,13 +219,10 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
-    per = {"amax": 0.0, "scales": 0.0, "quantize": 0.0, "attn_fp8": 0.0}
-    for e in evs:
-        per["amax"] += e[0].elapsed_time(e[1])
-        per["scales"] += e[1].elapsed_time(e[2])
-        per["quantize"] += e[2].elapsed_time(e[3])
-        per["attn_fp8"] += e[3].elapsed_time(e[4])
-    per = {k2: v2 / args.steps for k2, v2 in per.items()}       # ms per launch
+    names = ("amax", "scales", "quantize", "attn_fp8")
+    samples = {k2: [e[i].elapsed_time(e[i + 1]) for e in evs] for i, k2 in enumerate(names)}
+    per = {k2: sum(v2) / len(v2) for k2, v2 in samples.items()}            # ms per launch (mean)
+    per_median = {k2: sorted(v2)[len(v2) // 2] for k2, v2 in samples.items()}
 
     # BF16 skip-path kernel on the same batch
     for _ in range(args.warmup):
@@ -160,6 +235,8 @@ def main():
     e1.record()
     torch.cuda.synchronize()
     ms_bf16 = e0.elapsed_time(e1) / args.steps
+
+    cold = None if args.no_cold_quant else cold_quant(fa, w, q, k, v, cu_d, cu, st, ws, dev)
 
     attn_tflops = flops / (per["attn_fp8"] * 1e-3) / 1e12
     quant_gbs = (3 * n * 3) / (per["quantize"] * 1e-3) / 1e9
@@ -194,6 +271,7 @@ def main():
                      "traffic": traffic,
                      "algorithmic_per_launch": f"{flops:.4e} FLOP (4*S^2*d*H)"},
         "kernels_ms": {k2: round(v2, 5) for k2, v2 in per.items()},
+        "kernels_ms_median": {k2: round(v2, 5) for k2, v2 in per_median.items()},
         "attn_fp8_tflops": round(attn_tflops, 2),
         "attn_fp8_frac_fp8_peak": round(attn_tflops / FP8_PEAK_TFLOPS, 4),
         "attn_bf16_ms": round(ms_bf16, 5),
@@ -207,6 +285,8 @@ def main():
         "quant_algorithmic_bytes": f"{3 * n * 3:.4e} (2 B read + 1 B write per element, 3 tensors)",
         "amax_algorithmic_bytes": f"{3 * n * 2:.4e} (2 B read per element, 3 tensors)",
     }
+    if cold is not None:
+        result["quant_beyond_infinity_cache"] = cold
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, q, k, v, cu, args.cpu_rows)
     if args.copy_calibration_mib > 0:
