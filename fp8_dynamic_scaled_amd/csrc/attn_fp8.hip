@@ -40,9 +40,10 @@
 //   * the loop is unrolled by two so the two score register sets swap roles without
 //     copies; a ragged last tile is handled (masked) only in the epilogue;
 //   * K and V8t tiles go global -> LDS with buffer loads that write LDS directly (no VGPR
-//     staging, no ds_write), in three-stage rings, issued two tiles ahead of use; one
-//     vmcnt wait (all but the newest tile's loads) and one barrier per tile; 16-byte LDS
-//     chunks are XOR-swizzled so operand reads are conflict-free;
+//     staging, no ds_write), in four-stage rings; tiles move in pairs, with one vmcnt wait
+//     and one barrier per pair of tiles (waves drift apart by whole rescales between
+//     syncs), each pair's loads issued one pair ahead of use; 16-byte LDS chunks are
+//     XOR-swizzled so operand reads are conflict-free;
 //   * exp(x - m) * 448 is computed as exp2(s * c - (m * c - log2 448)), c = scales *
 //     log2(e): one FMA and one v_exp_f32 per score;
 //   * block -> work mapping is XCD-aware: consecutive work units (q-tiles of one
@@ -61,7 +62,7 @@ constexpr int kBN = FP8ATTN_KV_BLOCK;     // keys per tile = online-softmax bloc
 constexpr int kThreads = 256;
 constexpr int kKTileBytes = kBN * kHeadDim;   // K tile: 64 rows x 128 B
 constexpr int kVTileBytes = kHeadDim * kBN;   // V8t tile: 128 rows x 64 B
-constexpr int kStages = 3;                    // ring depth of each of K and V8t
+constexpr int kStages = 4;                    // ring depth of each of K and V8t
 constexpr uint32_t kOnesE4M3 = 0x38383838u;   // four E4M3 1.0
 constexpr int kBufferFlags = 0x00020000;      // raw buffer resource, dword 3 (gfx9)
 
@@ -253,9 +254,11 @@ void attn_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__
   uint8_t* const kst = smem;                                // K stage i at kst + i * kKTileBytes
   uint8_t* const vst = smem + kStages * kKTileBytes;        // V stage i at vst + i * kVTileBytes
   const int ntiles = (S + kBN - 1) / kBN;
-  // K tile j (clamped to the last tile, so the loads past the end stay in bounds and keep
-  // the per-tile load count uniform); rows at or past the end of the sequence read as 0
-  auto load_k = [&](int j, int stage) __attribute__((always_inline)) {
+  // K tile j into stage j % 4 (clamped to the last tile, so the loads past the end stay in
+  // bounds; they fill stages that are never read again); rows at or past the end of the
+  // sequence read as 0
+  auto load_k = [&](int j) __attribute__((always_inline)) {
+    const int stage = j & (kStages - 1);
     const int k0 = (j < ntiles ? j : ntiles - 1) * kBN;
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(kbase + (int64_t)k0 * row_stride), (short)0, (S - k0) * row_stride, kBufferFlags);
@@ -263,23 +266,26 @@ void attn_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)dst, 16, kvo0, 0, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(dst + 1024), 16, kvo1, 0, 0, 0);
   };
-  // V8t tile j (< ntiles): columns up to the sequence's 128-aligned padded length, which
-  // the quantise kernel zero-fills
-  auto load_v = [&](int j, int stage) __attribute__((always_inline)) {
+  // V8t tile j into stage j % 4 (clamped like K): columns up to the sequence's 128-aligned
+  // padded length, which the quantise kernel zero-fills
+  auto load_v = [&](int j) __attribute__((always_inline)) {
+    const int stage = j & (kStages - 1);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(vbase + j * kBN), (short)0, 0x7fffffff, kBufferFlags);
+        (void*)(vbase + (j < ntiles ? j : ntiles - 1) * kBN), (short)0, 0x7fffffff,
+        kBufferFlags);
     uint8_t* dst = vst + stage * kVTileBytes + wv * 2048;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)dst, 16, vvo0, 0, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(dst + 1024), 16, vvo1, 0, 0, 0);
   };
 
-  // ---- prologue loads: K(0), K(1), K(2), V(0) into stages 0, 1, 2, 0. From here on the
-  // newest four vector-memory operations of a thread are always the previous tile's K and
-  // V loads, so "vmcnt(4)" at the top of iteration t means K(t+1) and V(t-1) have landed.
-  load_k(0, 0);
-  load_k(1, 1);
-  load_k(2, 2);
-  load_v(0, 0);
+  // ---- prologue loads: everything iteration 0 and the first pair (tiles 1, 2) read:
+  // K(0) .. K(3), V(0), V(1). Tile j always lives in stage j % 4 of its ring.
+  load_k(0);
+  load_k(1);
+  load_k(2);
+  load_k(3);
+  load_v(0);
+  load_v(1);
 
   // ---- Q^T operand (B of S^T = K Q^T): lane = query n, 32 channel bytes of half g
   const int q_local = qt * kBM + wave * 32 + ln.n;
@@ -337,33 +343,33 @@ void attn_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__
     m_ref = m_prev;
   };
 
-  // Stage rotation: a = t % 3 (K(t) stage, where K(t+3) goes), b = (t+1) % 3 (K(t+1) to
-  // read, V(t+1) to load), cst = (t+2) % 3 = (t-1) % 3 (V(t-1) to read).
-  int sa = 0, sb = 1, sc = 2;
-  auto rotate = [&]() __attribute__((always_inline)) {
-    const int x = sa;
-    sa = sb;
-    sb = sc;
-    sc = x;
+  // Synchronisation of a pair of iterations t, t+1 (t odd). They read K(t+1), K(t+2),
+  // V(t-1), V(t), all loaded by the previous pair (or the prologue): wait for this
+  // thread's loads, then the barrier publishes everyone's. After it, the stages of K(t-1),
+  // K(t) and V(t-3), V(t-2) -- read only by the previous pair -- take the next pair's
+  // tiles K(t+3), K(t+4), V(t+1), V(t+2).
+  auto pair_sync = [&](int t) __attribute__((always_inline)) {
+    loads_barrier<0>();
+    load_k(t + 3);
+    load_k(t + 4);
+    load_v(t + 1);
+    load_v(t + 2);
   };
 
   // Iteration t < ntiles - 1: softmax of tile t (scores in cur), scores of tile t+1 into
-  // nxt, PV of tile t-1 (when t > 0). The stages being loaded (K stage t%3, last read by
-  // S(t) in iteration t-1; V stage (t+1)%3, last read by PV(t-2) in iteration t-1) are
-  // free once every wave has passed the barrier.
+  // nxt, PV of tile t-1 (when t > 0).
   auto iteration = [&](int t, v16f& cur0, v16f& cur1, v16f& nxt0, v16f& nxt1,
                        auto do_pv) __attribute__((always_inline)) {
     constexpr bool PV = decltype(do_pv)::value;
-    loads_barrier<4>();   // K(t+1), V(t-1) landed; only the previous tile's 4 loads pending
-    load_k(t + 3, sa);
-    load_v(t + 1, sb);
+    const int sk = (t + 1) & (kStages - 1);     // stage of K(t+1)
+    const int sv = (t - 1) & (kStages - 1);     // stage of V(t-1)
     if (PV) catch_up();
     // ---- one region, written in issue order: each MFMA is followed by one chunk of the
     // softmax (a part of the row maximum, or the exp/convert of 4 scores), and
     // sched_barrier(0) keeps every pair where it is, so the matrix core always has the
     // next MFMA queued while the vector ALU works through the chunk.
-    const uint8_t* vr = vst + sc * kVTileBytes + ln.n * kBN;        // V(t-1) row of lane
-    const uint8_t* kr0 = kst + sb * kKTileBytes + ln.n * kHeadDim;  // K(t+1) rows of lane
+    const uint8_t* vr = vst + sv * kVTileBytes + ln.n * kBN;        // V(t-1) row of lane
+    const uint8_t* kr0 = kst + sk * kKTileBytes + ln.n * kHeadDim;  // K(t+1) rows of lane
     const uint8_t* kr1 = kr0 + 32 * kHeadDim;
     const v16f zero16 = {};
     v8i va0, va1, va2, va3;
@@ -415,21 +421,26 @@ void attn_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__
     pin(p);
     p_prev = p;
     m_prev = m_cur;
-    rotate();
   };
   using T_ = std::true_type;
   using F_ = std::false_type;
 
-  // ---- main loop over t = 0 .. ntiles-2, unrolled by two (scores alternate a <-> b)
+  // ---- main loop over t = 0 .. ntiles-2 in pairs (scores alternate a <-> b). Iteration
+  // 0 reads only prologue tiles, which the barrier above published.
   int t = 0;
   if (ntiles > 1) {
     iteration(0, sa0, sa1, sb0, sb1, F_{});
     t = 1;
     for (; t + 2 < ntiles; t += 2) {
+      pair_sync(t);
       iteration(t, sb0, sb1, sa0, sa1, T_{});
       iteration(t + 1, sa0, sa1, sb0, sb1, T_{});
     }
     if (t + 1 < ntiles) {
+      // a last single iteration t = ntiles - 2: K(t+1), V(t-1) came with the previous
+      // pair; V(t+1) = V(ntiles-1) is still to load (for the epilogue)
+      loads_barrier<0>();
+      load_v(t + 1);
       iteration(t, sb0, sb1, sa0, sa1, T_{});
       ++t;
     } else {
@@ -437,11 +448,12 @@ void attn_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__
       sa1 = sb1;
     }
   }
-  // ---- epilogue: t = ntiles - 1, scores in set a
+  // ---- epilogue: t = ntiles - 1, scores in set a; V(ntiles-2), V(ntiles-1) loaded
   loads_barrier<0>();
   if (ntiles > 1) {
     catch_up();
-    pv(vst + sc * kVTileBytes, ln, p_prev, ones, rs, o0, o1, o2, o3);   // PV(ntiles-2)
+    pv(vst + ((ntiles - 2) & (kStages - 1)) * kVTileBytes, ln, p_prev, ones, rs, o0, o1, o2,
+       o3);   // PV(ntiles-2)
   }
   {
     const bool ragged = last_lim != kBN;
@@ -453,8 +465,8 @@ void attn_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__
     m_prev = m_cur;
   }
   catch_up();
-  // V(ntiles-1) is in stage (ntiles-1) % 3 = sa after the rotations above
-  pv(vst + sa * kVTileBytes, ln, p_prev, ones, rs, o0, o1, o2, o3);
+  pv(vst + ((ntiles - 1) & (kStages - 1)) * kVTileBytes, ln, p_prev, ones, rs, o0, o1, o2,
+     o3);   // PV(ntiles-1)
 
   // ---- O = O * scale_v / l, bf16, one query row per lane
   if (q_local < S) {

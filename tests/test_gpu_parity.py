@@ -205,7 +205,8 @@ def _assert_close(tag, got, want, max_tol=MAX_ABS_TOL, mean_tol=MEAN_ABS_TOL):
 
 @pytest.mark.parametrize("lens,H,outliers", [([300, 1, 77, 513, 0, 128, 64], 2, False),
                                              ([1000], 3, True), ([63, 65, 129, 191], 2, False),
-                                             ([1], 1, False), ([2049, 31], 2, True)])
+                                             ([1], 1, False), ([2049, 31], 2, True),
+                                             ([250, 200, 384, 320], 2, False)])
 def test_fp8_attention_all_rows(lens, H, outliers):
     say(f"fp8 attention lens={lens} H={H} outliers={outliers}")
     q, k, v, cu = random_varlen(lens, H, seed=len(lens) * 31 + H, device=DEV, outliers=outliers)
