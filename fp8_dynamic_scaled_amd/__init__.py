@@ -11,10 +11,13 @@ from .api import (AttentionLayer, DEFAULT_MARGIN, HEAD_DIM, KV_BLOCK, attend, de
                   split_workspace, state_bytes, state_reset, workspace_bytes)
 from ._lib import Fp8AttnError, LIB_PATH, load as load_library
 from .selectors import parse_selector, skip_fp8
+from . import scale_file
+from .scale_file import load_scale_file, save_scale_file, static_layers
 
 __all__ = [
     "AttentionLayer", "DEFAULT_MARGIN", "HEAD_DIM", "KV_BLOCK", "attend", "default_softmax_scale", "forward",
     "new_state", "observe_amax", "pad_start", "quantize", "read_state", "scales",
     "split_workspace", "state_bytes", "state_reset", "workspace_bytes", "Fp8AttnError",
     "LIB_PATH", "load_library", "parse_selector", "skip_fp8",
+    "scale_file", "load_scale_file", "save_scale_file", "static_layers",
 ]
