@@ -1,11 +1,14 @@
 """Benchmark of the FP8 attention hot path on one MI355X.
 
-One step = one FP8 attention call on a batch already resident in HBM: observe the Q/K/V
-amax (amax kernel), update the scales (scales kernel), quantise Q/K/V to E4M3 (quantise
-kernel) and run the FP8 flash-attention kernel -- four launches, exactly the FP8 path of
-fp8attn_forward preceded by the dynamic-scale update. The BF16 skip-path kernel is timed
-on the same batch afterwards (same-hardware baseline). Workload: the kernel point (one
-sequence of 8192 tokens, 16 heads, head_dim 128, bf16 N(0,1) with x20 outlier columns).
+One step = one dynamically scaled FP8 attention call on a batch already resident in HBM:
+observe the Q/K/V amax, update the 16-slot ring and the scales, quantise Q/K/V to E4M3
+(fp8attn_quantize_dynamic: a quantise pass that observes the amax while it quantises with
+the ring's other 15 slots, the scales kernel, and a re-quantise pass that exits at once
+unless the window maximum moved), then the FP8 flash-attention kernel (fp8attn_attend).
+The same kernels with the amax read as a pass of its own (observe, scales, plain quantise)
+are timed afterwards for reference, then the BF16 skip-path kernel on the same batch
+(same-hardware baseline). Workload: the kernel point (one sequence of 8192 tokens, 16
+heads, head_dim 128, bf16 N(0,1) with x20 outlier columns).
 
 Prints ONE JSON line. value = attention FLOPs of the step (4 * S^2 * d * H) / step time,
 in TFLOP/s. Per-kernel durations come from HIP events recorded on the stream the kernels
@@ -122,14 +125,26 @@ def cold_quant(fa, w, q, k, v, cu_d, cu, st, ws, dev, reps=10):
             tot["amax"] += ev[0].elapsed_time(ev[1]) / reps
             tot["quantize"] += ev[2].elapsed_time(ev[3]) / reps
             tot["step"] += ev[0].elapsed_time(ev[3]) / reps
+    one = 0.0
+    for r in range(reps + 2):
+        flush.fill_(r & 0xff)
+        ev[0].record()
+        fa.quantize_dynamic(st, q, k, v, cu_d, cu, workspace=ws)
+        ev[1].record()
+        torch.cuda.synchronize()
+        if r >= 2:
+            one += ev[0].elapsed_time(ev[1]) / reps
     out[w.name + "_flushed"] = {
+        "one_pass_dynamic_ms": round(one, 5),
+        "one_pass_dynamic_gbs": round(3 * n * 3 / (one * 1e-3) / 1e9, 1),
         "amax_ms": round(tot["amax"], 5), "quantize_ms": round(tot["quantize"], 5),
         "amax_scales_quantize_ms": round(tot["step"], 5),
         "quant_gbs": round(3 * n * 3 / (tot["quantize"] * 1e-3) / 1e9, 1),
         "amax_gbs": round(3 * n * 2 / (tot["amax"] * 1e-3) / 1e9, 1),
         "dynamic_path_gbs": round(3 * n * 5 / (tot["step"] * 1e-3) / 1e9, 1),
         "note": "512 MB device write before every launch; bytes: amax 2 B, quantise 3 B, "
-                "the dynamic path 5 B per element of Q, K, V"}
+                "the separate dynamic path 5 B, the one-pass dynamic path 3 B per element of "
+                "Q, K, V (the window maximum does not move between these repeats)"}
     del flush
     w4 = WORKLOADS["4k"]
     q4, k4, v4 = make_qkv(w4, 0, dev)
@@ -157,8 +172,17 @@ def cold_quant(fa, w, q, k, v, cu_d, cu, st, ws, dev, reps=10):
     am = sum(x[0].elapsed_time(x[1]) for x in e) / reps
     qm = sum(x[2].elapsed_time(x[3]) for x in e) / reps
     sm = sum(x[0].elapsed_time(x[3]) for x in e) / reps
+    for r in range(reps):
+        e[r][0].record()
+        fa.quantize_dynamic(st4, q4, k4, v4, cu4_d, cu4, workspace=ws4)
+        e[r][1].record()
+    torch.cuda.synchronize()
+    om = sum(x[0].elapsed_time(x[1]) for x in e) / reps
     out["4k"] = {
-        "elements_per_tensor": n4, "amax_ms": round(am, 5), "quantize_ms": round(qm, 5),
+        "elements_per_tensor": n4,
+        "one_pass_dynamic_ms": round(om, 5),
+        "one_pass_dynamic_gbs": round(3 * n4 * 3 / (om * 1e-3) / 1e9, 1),
+        "amax_ms": round(am, 5), "quantize_ms": round(qm, 5),
         "amax_scales_quantize_ms": round(sm, 5),
         "quant_gbs": round(3 * n4 * 3 / (qm * 1e-3) / 1e9, 1),
         "amax_gbs": round(3 * n4 * 2 / (am * 1e-3) / 1e9, 1),
@@ -196,22 +220,25 @@ def main():
     def step(ev=None):
         if ev is not None:
             ev[0].record()
-        fa.observe_amax(st, q, k, v)
+        fa.quantize_dynamic(st, q, k, v, cu_d, cu, workspace=ws)
         if ev is not None:
             ev[1].record()
-        fa.scales(st, "dynamic")
-        if ev is not None:
-            ev[2].record()
-        fa.quantize(st, q, k, v, cu_d, cu, workspace=ws)
-        if ev is not None:
-            ev[3].record()
         fa.attend(st, ws, cu_d, cu, H, out=out)
         if ev is not None:
-            ev[4].record()
+            ev[2].record()
+
+    def separate(ev):
+        ev[0].record()
+        fa.observe_amax(st, q, k, v)
+        ev[1].record()
+        fa.scales(st, "dynamic")
+        ev[2].record()
+        fa.quantize(st, q, k, v, cu_d, cu, workspace=ws)
+        ev[3].record()
 
     for _ in range(args.warmup):
         step()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -219,8 +246,17 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
-    names = ("amax", "scales", "quantize", "attn_fp8")
+    names = ("quantize_dynamic", "attn_fp8")
     samples = {k2: [e[i].elapsed_time(e[i + 1]) for e in evs] for i, k2 in enumerate(names)}
+
+    # reference: the same step with the amax read as a pass of its own
+    sev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        separate(sev[i])
+        fa.attend(st, ws, cu_d, cu, H, out=out)
+    torch.cuda.synchronize()
+    for i, k2 in enumerate(("amax", "scales", "quantize")):
+        samples[k2] = [e[i].elapsed_time(e[i + 1]) for e in sev]
     per = {k2: sum(v2) / len(v2) for k2, v2 in samples.items()}            # ms per launch (mean)
     per_median = {k2: sorted(v2)[len(v2) // 2] for k2, v2 in samples.items()}
 
@@ -240,6 +276,7 @@ def main():
 
     attn_tflops = flops / (per["attn_fp8"] * 1e-3) / 1e12
     quant_gbs = (3 * n * 3) / (per["quantize"] * 1e-3) / 1e9
+    dyn_gbs = (3 * n * 3) / (per["quantize_dynamic"] * 1e-3) / 1e9
     amax_gbs = (3 * n * 2) / (per["amax"] * 1e-3) / 1e9
     bf16_tflops = flops / (ms_bf16 * 1e-3) / 1e12
 
@@ -279,6 +316,9 @@ def main():
         "attn_bf16_frac_bf16_peak": round(bf16_tflops / BF16_PEAK_TFLOPS, 4),
         "fp8_over_bf16_speedup": round(ms_bf16 / per["attn_fp8"], 3),
         "quant_gbs": round(quant_gbs, 1),
+        "dynamic_quant_gbs": round(dyn_gbs, 1),
+        "dynamic_quant_note": "fp8attn_quantize_dynamic (quantise + observe, scales, "
+                              "re-quantise check): 3 B per element of Q, K, V over its time",
         "quant_frac_hbm_peak": round(quant_gbs / HBM_PEAK_GBS, 4),
         "amax_gbs": round(amax_gbs, 1),
         "amax_frac_hbm_peak": round(amax_gbs / HBM_PEAK_GBS, 4),

@@ -16,6 +16,7 @@ FP8ATTN_EHIP = -3
 FP8ATTN_DYNAMIC = 0
 FP8ATTN_STATIC = 1
 FP8ATTN_SKIP = 1
+FP8ATTN_OBSERVE = 2
 
 _c_void_p = ctypes.c_void_p
 _i32p = ctypes.POINTER(ctypes.c_int32)
@@ -34,6 +35,10 @@ SIGNATURES = {
     "fp8attn_quantize": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                         _i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                         _c_void_p, ctypes.c_size_t, _c_void_p]),
+    "fp8attn_quantize_dynamic": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                                _c_void_p, _i32p, ctypes.c_int, ctypes.c_int,
+                                                ctypes.c_int, _c_void_p, ctypes.c_size_t,
+                                                _c_void_p]),
     "fp8attn_forward": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                        _i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                        ctypes.c_float, ctypes.c_uint, _c_void_p,

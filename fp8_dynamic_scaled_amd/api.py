@@ -13,7 +13,7 @@ import numpy as np
 import torch
 
 from . import _lib
-from ._lib import FP8ATTN_DYNAMIC, FP8ATTN_SKIP, FP8ATTN_STATIC, check
+from ._lib import FP8ATTN_DYNAMIC, FP8ATTN_OBSERVE, FP8ATTN_SKIP, FP8ATTN_STATIC, check
 
 HEAD_DIM = 128
 DEFAULT_MARGIN = 1.5
@@ -143,6 +143,26 @@ def quantize(state, q, k, v, cu_seqlens, cu_seqlens_host=None,
     return workspace
 
 
+def quantize_dynamic(state, q, k, v, cu_seqlens, cu_seqlens_host=None,
+                     workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One dynamic forward's observe + ring + scales + quantise (fp8attn_quantize_dynamic):
+    the same state and workspace bytes as observe_amax, scales("dynamic") and quantize,
+    reading Q/K/V once when the window maximum does not move. Returns the workspace."""
+    host, T, H, D = _varlen_args(q, k, v, cu_seqlens, cu_seqlens_host)
+    B = host.shape[0] - 1
+    need = workspace_bytes(T, B, H, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _need_cuda("state", state, torch.uint8)
+    _need_cuda("workspace", workspace, torch.uint8)
+    check("fp8attn_quantize_dynamic",
+          _lib.load().fp8attn_quantize_dynamic(_ptr(state), _ptr(q), _ptr(k), _ptr(v),
+                                               _ptr(cu_seqlens), host.ctypes.data_as(_lib._i32p),
+                                               B, H, D, _ptr(workspace), workspace.numel(),
+                                               _stream(q.device)))
+    return workspace
+
+
 def split_workspace(workspace: torch.Tensor, total_tokens: int, num_seqs: int, num_heads: int,
                     head_dim: int = HEAD_DIM):
     """Views (q8 [T,H,D], k8 [T,H,D], v8t [H,D,Tp]) of a workspace (uint8)."""
@@ -183,8 +203,12 @@ def attend(state, workspace, cu_seqlens, cu_seqlens_host, num_heads: int,
 
 def forward(state, q, k, v, cu_seqlens, cu_seqlens_host=None, softmax_scale: float = 0.0,
             skip: bool = False, workspace: Optional[torch.Tensor] = None,
-            out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Varlen attention forward; FP8 path unless skip (then the BF16 kernel)."""
+            out: Optional[torch.Tensor] = None, observe: bool = False) -> torch.Tensor:
+    """Varlen attention forward; FP8 path unless skip (then the BF16 kernel). With
+    observe=True the FP8 path first does the dynamic observe + ring + scales update itself
+    (FP8ATTN_OBSERVE)."""
+    if skip and observe:
+        raise ValueError("observe applies to the FP8 path only")
     host, T, H, D = _varlen_args(q, k, v, cu_seqlens, cu_seqlens_host)
     B = host.shape[0] - 1
     if out is None:
@@ -202,7 +226,7 @@ def forward(state, q, k, v, cu_seqlens, cu_seqlens_host=None, softmax_scale: flo
             workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
         _need_cuda("workspace", workspace, torch.uint8)
         ws_n = workspace.numel()
-    flags = FP8ATTN_SKIP if skip else 0
+    flags = (FP8ATTN_SKIP if skip else 0) | (FP8ATTN_OBSERVE if observe else 0)
     check("fp8attn_forward",
           _lib.load().fp8attn_forward(_ptr(state), _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens),
                                       host.ctypes.data_as(_lib._i32p), B, H, D,
@@ -216,13 +240,18 @@ class AttentionLayer:
     """FP8 attention state of one attention layer.
 
     Dynamic (default): every FP8 forward observes the Q/K/V amax and updates the layer's
-    16-slot ring before quantising. Static: pass static_amax = calibrated (q, k, v) amax;
+    16-slot ring before quantising -- by default in one pass over Q/K/V
+    (fp8attn_quantize_dynamic, identical bytes); one_pass=False issues the separate
+    observe, scales and quantise calls instead. Static: pass static_amax = calibrated
+    (q, k, v) amax;
     the scale is amax * margin / 448 and nothing is observed. A forward with skip=True runs
     the BF16 kernel and leaves the state untouched.
     """
 
-    def __init__(self, device=None, static_amax=None, margin: float = DEFAULT_MARGIN):
+    def __init__(self, device=None, static_amax=None, margin: float = DEFAULT_MARGIN,
+                 one_pass: bool = True):
         self.state = new_state(device)
+        self.one_pass = bool(one_pass)
         self.static_amax = None if static_amax is None else [float(x) for x in static_amax]
         self.margin = float(margin)
         self._ws = None
@@ -239,12 +268,15 @@ class AttentionLayer:
             return forward(None, q, k, v, cu_seqlens, cu_seqlens_host, softmax_scale, True,
                            None, out)
         host = _cu_host(cu_seqlens, cu_seqlens_host)
+        ws = self.workspace(q.shape[0], host.shape[0] - 1, q.shape[1], q.device)
         if self.static_amax is None:
+            if self.one_pass:
+                return forward(self.state, q, k, v, cu_seqlens, host, softmax_scale, False, ws,
+                               out, observe=True)
             observe_amax(self.state, q, k, v)
             scales(self.state, "dynamic")
         else:
             scales(self.state, "static", self.static_amax, self.margin)
-        ws = self.workspace(q.shape[0], host.shape[0] - 1, q.shape[1], q.device)
         return forward(self.state, q, k, v, cu_seqlens, host, softmax_scale, False, ws, out)
 
 

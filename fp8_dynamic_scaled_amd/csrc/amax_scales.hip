@@ -102,10 +102,9 @@ __global__ void scales_kernel(fp8attn_state* st, int mode, float s0, float s1, f
       const float cal = t == 0 ? s0 : (t == 1 ? s1 : s2);
       A = cal * margin;
     }
-    const float a_eff = __builtin_fmaxf(A, 0x1p-64f);
     st->amax[t] = A;
-    st->scale[t] = a_eff / kE4M3Max;
-    st->inv_scale[t] = kE4M3Max / a_eff;
+    st->scale[t] = scale_from_amax(A);
+    st->inv_scale[t] = inv_scale_from_amax(A);
     st->cur[t] = 0u;
   }
   __syncthreads();

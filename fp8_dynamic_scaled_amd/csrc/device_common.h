@@ -32,6 +32,17 @@ __device__ __forceinline__ int cvt_pk_e4m3(float a, float b, int old) {
   return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, HI);
 }
 
+// Per-tensor scale pair from the window (or static) amax A: scale = A/448, inv = 448/A,
+// both by IEEE division, with A floored at 2^-64 so that an all-zero tensor still gets a
+// finite inverse. Every kernel that turns an A into a scale uses these.
+constexpr float kAmaxFloor = 0x1p-64f;
+__device__ __forceinline__ float scale_from_amax(float A) {
+  return __builtin_fmaxf(A, kAmaxFloor) / kE4M3Max;
+}
+__device__ __forceinline__ float inv_scale_from_amax(float A) {
+  return kE4M3Max / __builtin_fmaxf(A, kAmaxFloor);
+}
+
 __device__ __forceinline__ float clamp_e4m3(float y) {
   return __builtin_fminf(__builtin_fmaxf(y, -kE4M3Max), kE4M3Max);
 }

@@ -55,7 +55,6 @@ struct Varlen {
 int check_varlen(const char* fn, const void* q, const void* k, const void* v,
                  const int32_t* cu, const int32_t* cu_host, int num_seqs, int num_heads,
                  int head_dim, Varlen* out) {
-  if (!q || !k || !v) return fail(FP8ATTN_EINVAL, "%s: q, k and v must be non-NULL", fn);
   if (!cu || !cu_host)
     return fail(FP8ATTN_EINVAL, "%s: cu_seqlens and cu_seqlens_host must be non-NULL", fn);
   if (num_seqs < 1) return fail(FP8ATTN_EINVAL, "%s: num_seqs must be >= 1 (got %d)", fn, num_seqs);
@@ -74,6 +73,8 @@ int check_varlen(const char* fn, const void* q, const void* k, const void* v,
     if (len > max_len) max_len = (int)len;
   }
   const int64_t T = cu_host[num_seqs];
+  // an empty batch reads no tensor element: q, k, v may then be NULL
+  if (T > 0 && (!q || !k || !v)) return fail(FP8ATTN_EINVAL, "%s: q, k and v must be non-NULL", fn);
   // token indices and per-head element offsets are kept in 32/64-bit ranges
   if (T * num_heads > ((int64_t)1 << 31) - 1)
     return fail(FP8ATTN_EINVAL, "%s: total_tokens * num_heads = %lld exceeds 2^31-1", fn,
@@ -182,6 +183,34 @@ int fp8attn_quantize(const void* state, const void* q, const void* k, const void
       fn);
 }
 
+int fp8attn_quantize_dynamic(void* state, const void* q, const void* k, const void* v,
+                             const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+                             int num_seqs, int num_heads, int head_dim, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  const char* fn = "fp8attn_quantize_dynamic";
+  if (!state) return fail(FP8ATTN_EINVAL, "%s: state must be non-NULL", fn);
+  Varlen vl;
+  int rc = check_varlen(fn, q, k, v, cu_seqlens, cu_seqlens_host, num_seqs, num_heads, head_dim, &vl);
+  if (rc != FP8ATTN_OK) return rc;
+  if (!workspace || !aligned16(workspace))
+    return fail(FP8ATTN_EINVAL, "%s: workspace must be non-NULL and 16-byte aligned", fn);
+  if (workspace_bytes < vl.ws_bytes)
+    return fail(FP8ATTN_EINVAL, "%s: workspace of %zu bytes is smaller than the %zu needed", fn,
+                workspace_bytes, vl.ws_bytes);
+  fp8attn_state* st = static_cast<fp8attn_state*>(state);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // no tokens: the observation is 0 and only the ring moves, as with observe + scales
+  if (vl.T == 0) return hip_status(fp8attn::launch_scales(st, FP8ATTN_DYNAMIC, nullptr, 0.0f, s), fn);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  const int64_t n = vl.T * num_heads * head_dim;
+  return hip_status(
+      fp8attn::launch_quantize_dynamic(st, static_cast<const uint16_t*>(q),
+                                       static_cast<const uint16_t*>(k),
+                                       static_cast<const uint16_t*>(v), cu_seqlens, num_seqs,
+                                       vl.T, num_heads, ws, ws + n, ws + 2 * n, vl.Tp, s),
+      fn);
+}
+
 int fp8attn_attend(const void* state, const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
                    int num_seqs, int num_heads, int head_dim, float softmax_scale,
                    const void* workspace, size_t workspace_bytes, void* out, void* stream) {
@@ -219,16 +248,19 @@ int fp8attn_attend(const void* state, const int32_t* cu_seqlens, const int32_t* 
                     fn);
 }
 
-int fp8attn_forward(const void* state, const void* q, const void* k, const void* v,
+int fp8attn_forward(void* state, const void* q, const void* k, const void* v,
                     const int32_t* cu_seqlens, const int32_t* cu_seqlens_host, int num_seqs,
                     int num_heads, int head_dim, float softmax_scale, unsigned flags,
                     void* workspace, size_t workspace_bytes, void* out, void* stream) {
   const char* fn = "fp8attn_forward";
-  if (flags & ~FP8ATTN_SKIP) return fail(FP8ATTN_EINVAL, "%s: unknown flag bits 0x%x", fn, flags);
+  if (flags & ~(FP8ATTN_SKIP | FP8ATTN_OBSERVE))
+    return fail(FP8ATTN_EINVAL, "%s: unknown flag bits 0x%x", fn, flags);
+  if ((flags & FP8ATTN_SKIP) && (flags & FP8ATTN_OBSERVE))
+    return fail(FP8ATTN_EINVAL, "%s: FP8ATTN_OBSERVE and FP8ATTN_SKIP exclude each other", fn);
   Varlen vl;
   int rc = check_varlen(fn, q, k, v, cu_seqlens, cu_seqlens_host, num_seqs, num_heads, head_dim, &vl);
   if (rc != FP8ATTN_OK) return rc;
-  if (!out || !aligned16(out))
+  if ((vl.T > 0 && !out) || !aligned16(out))
     return fail(FP8ATTN_EINVAL, "%s: out must be non-NULL and 16-byte aligned", fn);
   if (!std::isfinite(softmax_scale))
     return fail(FP8ATTN_EINVAL, "%s: softmax_scale must be finite", fn);
@@ -241,10 +273,16 @@ int fp8attn_forward(const void* state, const void* q, const void* k, const void*
       return fail(FP8ATTN_EINVAL, "%s: workspace of %zu bytes is smaller than the %zu needed",
                   fn, workspace_bytes, vl.ws_bytes);
   }
-  if (vl.T == 0) return ok();
+  const bool observe = (flags & FP8ATTN_OBSERVE) != 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (vl.T == 0) {
+    if (!observe) return ok();
+    return hip_status(fp8attn::launch_scales(static_cast<fp8attn_state*>(state), FP8ATTN_DYNAMIC,
+                                             nullptr, 0.0f, s),
+                      fn);
+  }
   const float sm = softmax_scale > 0.0f ? softmax_scale
                                         : (float)(1.0 / std::sqrt((double)head_dim));
-  hipStream_t s = static_cast<hipStream_t>(stream);
   fp8attn::AttnLaunch a;
   a.cu = cu_seqlens;
   a.num_seqs = num_seqs;
@@ -263,10 +301,15 @@ int fp8attn_forward(const void* state, const void* q, const void* k, const void*
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   const int64_t n = vl.T * num_heads * head_dim;
   const fp8attn_state* st = static_cast<const fp8attn_state*>(state);
-  hipError_t e = fp8attn::launch_quantize(st, static_cast<const uint16_t*>(q),
-                                          static_cast<const uint16_t*>(k),
-                                          static_cast<const uint16_t*>(v), cu_seqlens, num_seqs,
-                                          vl.T, num_heads, ws, ws + n, ws + 2 * n, vl.Tp, s);
+  const uint16_t* q16 = static_cast<const uint16_t*>(q);
+  const uint16_t* k16 = static_cast<const uint16_t*>(k);
+  const uint16_t* v16 = static_cast<const uint16_t*>(v);
+  hipError_t e =
+      observe ? fp8attn::launch_quantize_dynamic(static_cast<fp8attn_state*>(state), q16, k16, v16,
+                                                 cu_seqlens, num_seqs, vl.T, num_heads, ws,
+                                                 ws + n, ws + 2 * n, vl.Tp, s)
+              : fp8attn::launch_quantize(st, q16, k16, v16, cu_seqlens, num_seqs, vl.T,
+                                         num_heads, ws, ws + n, ws + 2 * n, vl.Tp, s);
   if (e != hipSuccess) return hip_status(e, "fp8attn_forward (quantise)");
   return hip_status(fp8attn::launch_attn_fp8(a, st, ws, ws + n, ws + 2 * n, s),
                     "fp8attn_forward (attention)");

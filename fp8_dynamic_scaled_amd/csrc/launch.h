@@ -23,6 +23,15 @@ hipError_t launch_quantize(const fp8attn_state* st, const uint16_t* q, const uin
                            int H, uint8_t* q8, uint8_t* k8, uint8_t* v8t, int64_t Tp,
                            hipStream_t s);
 
+// Dynamic forward in one pass over Q/K/V when the window maximum does not move: quantise
+// with the scale of the ring's other 15 slots while observing this forward's amax, run the
+// scales kernel (dynamic), then re-quantise the tensors whose window maximum changed. The
+// state's pending observation (cur) must be clear, as every scales call leaves it.
+hipError_t launch_quantize_dynamic(fp8attn_state* st, const uint16_t* q, const uint16_t* k,
+                                   const uint16_t* v, const int32_t* cu, int num_seqs,
+                                   int64_t T, int H, uint8_t* q8, uint8_t* k8, uint8_t* v8t,
+                                   int64_t Tp, hipStream_t s);
+
 struct AttnLaunch {
   const int32_t* cu;     // device cu_seqlens
   int num_seqs;

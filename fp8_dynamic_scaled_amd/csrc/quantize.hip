@@ -1,16 +1,31 @@
 // Per-tensor BF16 -> E4M3 quantisation of Q, K and V in one launch (vLLM-Omni "Quantized
 // KV Cache", "Overview": Q/K/V are quantised on the fly right before the attention
-// operator; vLLM docs "FP8 ViT Encoder Attention": per-tensor scales).
+// operator; vLLM docs "FP8 ViT Encoder Attention": per-tensor scales, and in "Usage" the
+// dynamic mode whose 16-slot amax ring drives every forward's scale).
 //
 // q8 = E4M3(fp32(x * inv_scale[t])): one IEEE fp32 multiply, a clamp to +-448 (the
 // converter would turn values beyond 464 into NaN), then the hardware RNE converter.
 //
-// Blocks [0, nb_qk) stream Q and K element-wise into [T][H][D] (16 bytes in, 8 out per
-// thread step). Blocks [nb_qk, nb_qk + nb_v) each take one head and one 128-column tile
-// of the padded key axis of V8t [H][D][Tp] (see fp8attn.h): they load 128 tokens x 128
-// channels of V, quantise, transpose through LDS and write 128 channel rows of 128
-// contiguous key bytes. Columns outside every sequence are written as 0 so the
-// attention kernel can read whole tiles without bounds checks on V.
+// Work split (grid-stride, so the grid stays small whatever the batch): blocks
+// [0, nb_qk) stream Q and K element-wise into [T][H][D] (four 16-byte groups in flight
+// per thread); blocks [nb_qk, nb_qk + nb_v) walk (head, 128-column tile) pairs of the
+// padded key axis of V8t [H][D][Tp] (see fp8attn.h): each loads 128 tokens x 128
+// channels of V, quantises, transposes through LDS and writes 128 channel rows of 128
+// contiguous key bytes. Columns outside every sequence are written as 0 so the attention
+// kernel can read whole tiles without bounds checks on V.
+//
+// Three modes share that kernel:
+//  * kPlain: scale from the state (written by the scales kernel).
+//  * kObserve (speculative dynamic forward): this forward's window maximum will be
+//    A = max(A_pred, amax), A_pred = max of the ring slots other than the one its
+//    observation replaces. The kernel quantises with A_pred's scale and, in the same pass
+//    over the input, observes amax into the state's pending slot (as the amax kernel
+//    does). The scales kernel then runs as usual.
+//  * kRedo (after the scales kernel): recomputes A_pred from the ring (every slot but the
+//    one just written) and re-quantises a tensor only when its final A differs, i.e. when
+//    this forward's amax is a new window maximum; otherwise its blocks return at once.
+// The bytes are therefore exactly those of amax + scales + plain quantise, while in steady
+// state Q, K and V are read once instead of twice.
 #include "device_common.h"
 #include "launch.h"
 
@@ -19,10 +34,16 @@ namespace fp8attn {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kQkPerThread = 2;                                 // uint4 groups per thread
-constexpr int kQkPerBlock = kThreads * kQkPerThread * 8;        // elements per block
+constexpr int kQkGroups = 4;                                    // 8-element groups per thread step
 constexpr int kVTile = 128;                                     // keys per V tile
 constexpr int kLdsRow = kVTile + 16;                            // bytes per LDS row (16B aligned)
+constexpr int kMaxBlocksPerPart = 1024;                         // Q/K blocks, V blocks
+// The re-quantise pass usually has nothing to do and its blocks return at once, so its
+// grid is kept small (its cost is then mostly the launch); when it does work -- the first
+// forward of a layer, or a new window maximum -- the grid-stride loops cover everything.
+constexpr int kMaxRedoBlocksPerPart = 128;
+
+enum QuantMode { kPlain = 0, kObserve = 1, kRedo = 2 };
 
 __device__ __forceinline__ uint2 quant8(uint4 r, float inv) {
   // 8 bf16 -> 8 E4M3 bytes, element order preserved
@@ -39,87 +60,200 @@ __device__ __forceinline__ float bf16_at(const uint4& r, int c) {
   return (c & 1) ? bf16_hi(w) : bf16_lo(w);
 }
 
+// max of |x| over 8 packed bf16, as the 16-bit pattern with the sign cleared (which orders
+// like the magnitude), folded into m
+__device__ __forceinline__ uint32_t absmax8(uint32_t m, const uint4& r) {
+  us2 a = {(unsigned short)(m), (unsigned short)(m)};
+  const uint32_t w[4] = {r.x & 0x7fff7fffu, r.y & 0x7fff7fffu, r.z & 0x7fff7fffu,
+                         r.w & 0x7fff7fffu};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) a = __builtin_elementwise_max(a, *reinterpret_cast<const us2*>(&w[i]));
+  return a.x > a.y ? a.x : a.y;
+}
+
+// Largest ring entry of tensor t other than slot `skip`: the window maximum that this
+// forward's observation (in slot `skip`) can only raise.
+__device__ __forceinline__ float ring_max_except(const fp8attn_state* st, int t, uint32_t skip) {
+  float a = 0.0f;
+#pragma unroll
+  for (int s = 0; s < FP8ATTN_RING_SLOTS; ++s)
+    if ((uint32_t)s != skip) a = __builtin_fmaxf(a, st->ring[t][s]);
+  return a;
+}
+
+// Block-wide max of per-thread 16-bit magnitudes; thread 0 folds the result into the
+// pending observation state->cur[t] (fp32 bit image; a plain load first filters the blocks
+// that cannot raise it, since atomics on one address serialise in L2).
+__device__ __forceinline__ void publish_max(fp8attn_state* st, int t, uint32_t m, uint32_t* red) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const uint32_t o = __shfl_xor(m, off);
+    m = o > m ? o : m;
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();                          // red may still be read from a previous call
+  if (lane == 0) red[wave] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t b = red[0];
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; ++w) b = red[w] > b ? red[w] : b;
+    const uint32_t img = b << 16;
+    if (img != 0 && img > __hip_atomic_load(&st->cur[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+      atomicMax(&st->cur[t], img);
+  }
+}
+
+template <int MODE>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(
-    const fp8attn_state* __restrict__ st, const uint16_t* __restrict__ q,
+    fp8attn_state* __restrict__ st, const uint16_t* __restrict__ q,
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ cu, int num_seqs, int64_t n, int H, uint8_t* __restrict__ q8,
-    uint8_t* __restrict__ k8, uint8_t* __restrict__ v8t, int64_t Tp, int nb_qk) {
+    uint8_t* __restrict__ k8, uint8_t* __restrict__ v8t, int64_t Tp, int nb_qk, int nb_v) {
   __shared__ __attribute__((aligned(16))) uint8_t tile[kHeadDim * kLdsRow];
+  __shared__ uint32_t red[kThreads / 64];
   const int tid = threadIdx.x;
+
+  // ---- the scale of each tensor, and (re-quantise mode) which tensors need the work
+  float inv[3];
+  bool work[3] = {true, true, true};
+  if (MODE == kObserve) {
+    const uint32_t slot = st->count % FP8ATTN_RING_SLOTS;
+#pragma unroll
+    for (int t = 0; t < 3; ++t) inv[t] = inv_scale_from_amax(ring_max_except(st, t, slot));
+  } else {
+#pragma unroll
+    for (int t = 0; t < 3; ++t) inv[t] = st->inv_scale[t];
+    if (MODE == kRedo) {
+      const uint32_t slot = (st->count - 1u) % FP8ATTN_RING_SLOTS;   // just written
+#pragma unroll
+      for (int t = 0; t < 3; ++t) work[t] = st->amax[t] != ring_max_except(st, t, slot);
+    }
+  }
+
   if ((int)blockIdx.x < nb_qk) {
     // ---- Q and K: element-wise stream over the concatenation [Q | K] of 2n elements
-    const float inv_q = st->inv_scale[0];
-    const float inv_k = st->inv_scale[1];
-    const int64_t base = (int64_t)blockIdx.x * kQkPerBlock;
+    if (MODE == kRedo && !work[0] && !work[1]) return;
+    const int64_t groups = 2 * n / 8;                 // n is a multiple of 128
+    const int64_t step = (int64_t)nb_qk * kThreads * kQkGroups;
+    uint32_t mq = 0, mk = 0;
+    for (int64_t g0 = (int64_t)blockIdx.x * kThreads * kQkGroups; g0 < groups; g0 += step) {
+      uint4 r[kQkGroups];
 #pragma unroll
-    for (int u = 0; u < kQkPerThread; ++u) {
-      const int64_t e = base + ((int64_t)u * kThreads + tid) * 8;
-      if (e >= 2 * n) break;
-      const bool is_k = e >= n;                 // n is a multiple of 128: no group straddles
-      const int64_t off = is_k ? e - n : e;
-      const uint4 r = *reinterpret_cast<const uint4*>((is_k ? k : q) + off);
-      const uint2 o = quant8(r, is_k ? inv_k : inv_q);
-      *reinterpret_cast<uint2*>((is_k ? k8 : q8) + off) = o;
+      for (int u = 0; u < kQkGroups; ++u) {
+        const int64_t g = g0 + u * kThreads + tid;
+        if (g < groups) {
+          const int64_t e = g * 8;
+          const bool is_k = e >= n;
+          r[u] = *reinterpret_cast<const uint4*>((is_k ? k : q) + (is_k ? e - n : e));
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kQkGroups; ++u) {
+        const int64_t g = g0 + u * kThreads + tid;
+        if (g < groups) {
+          const int64_t e = g * 8;
+          const bool is_k = e >= n;
+          if (MODE == kObserve) {
+            if (is_k) mk = absmax8(mk, r[u]);
+            else mq = absmax8(mq, r[u]);
+          }
+          if (MODE != kRedo || work[is_k ? 1 : 0]) {
+            const uint2 o = quant8(r[u], inv[is_k ? 1 : 0]);
+            *reinterpret_cast<uint2*>((is_k ? k8 : q8) + (is_k ? e - n : e)) = o;
+          }
+        }
+      }
+    }
+    if (MODE == kObserve) {
+      publish_max(st, 0, mq, red);
+      publish_max(st, 1, mk, red);
     }
     return;
   }
-  // ---- V: one (padded key tile, head)
-  const float inv_v = st->inv_scale[2];
-  const int vb = (int)blockIdx.x - nb_qk;
-  const int h = vb % H;
-  const int64_t col0 = (int64_t)(vb / H) * kVTile;  // first padded key column of the tile
-  // sequence whose padded region holds col0: largest i with pad_start(i) <= col0
-  int lo = 0, hi = num_seqs - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (pad_start(cu[mid], mid) <= col0) lo = mid; else hi = mid - 1;
-  }
-  const int seq = lo;
-  const int64_t seq_begin = cu[seq];
-  const int64_t seq_len = (int64_t)cu[seq + 1] - seq_begin;
-  const int64_t j0 = col0 - pad_start(seq_begin, seq);  // key offset inside the sequence
 
-  // thread -> 4 consecutive keys x 16 channels; 8 threads cover one 256-byte token row
+  // ---- V: (padded key tile, head) pairs, grid-stride
+  if (MODE == kRedo && !work[2]) return;
+  const float inv_v = inv[2];
+  const int64_t tiles = (Tp / kVTile) * H;
   const int cc = tid & 7;           // channel chunk: channels 16cc .. 16cc+15
   const int kg = tid >> 3;          // key group: keys 4kg .. 4kg+3 of the tile
-  float x[4][16];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int64_t j = j0 + 4 * kg + r;
-    if (j < seq_len) {
-      const uint16_t* src = v + ((seq_begin + j) * H + h) * kHeadDim + 16 * cc;
-      const uint4 a = *reinterpret_cast<const uint4*>(src);
-      const uint4 b = *reinterpret_cast<const uint4*>(src + 8);
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        x[r][c] = clamp_e4m3(bf16_at(a, c) * inv_v);
-        x[r][8 + c] = clamp_e4m3(bf16_at(b, c) * inv_v);
-      }
-    } else {
-#pragma unroll
-      for (int c = 0; c < 16; ++c) x[r][c] = 0.0f;
+  uint32_t mv = 0;
+  for (int64_t vb = (int64_t)blockIdx.x - nb_qk; vb < tiles; vb += nb_v) {
+    const int h = (int)(vb % H);
+    const int64_t col0 = (vb / H) * kVTile;          // first padded key column of the tile
+    // sequence whose padded region holds col0: largest i with pad_start(i) <= col0
+    int lo = 0, hi = num_seqs - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (pad_start(cu[mid], mid) <= col0) lo = mid; else hi = mid - 1;
     }
-  }
-  // Transpose through LDS: row = channel, one dword = 4 keys of one channel. The dword
-  // column is XORed with 4 * (row / 16) so that the 8 channel chunks of a wave land in
-  // different banks; 16-byte chunks stay contiguous (chunk' = chunk ^ (row / 16)).
+    const int seq = lo;
+    const int64_t seq_begin = cu[seq];
+    const int64_t seq_len = (int64_t)cu[seq + 1] - seq_begin;
+    const int64_t j0 = col0 - pad_start(seq_begin, seq);  // key offset inside the sequence
+
+    // thread -> 4 consecutive keys x 16 channels; 8 threads cover one 256-byte token row
+    float x[4][16];
 #pragma unroll
-  for (int c = 0; c < 16; ++c) {
-    int w = cvt_pk_e4m3<false>(x[0][c], x[1][c], 0);
-    w = cvt_pk_e4m3<true>(x[2][c], x[3][c], w);
-    const int row = 16 * cc + c;
-    *reinterpret_cast<int*>(&tile[row * kLdsRow + 4 * (kg ^ (4 * cc))]) = w;
-  }
-  __syncthreads();
-  // write 128 rows x 128 bytes: 8 threads per row, 16 bytes each, 4 rows per thread
+    for (int r = 0; r < 4; ++r) {
+      const int64_t j = j0 + 4 * kg + r;
+      if (j < seq_len) {
+        const uint16_t* src = v + ((seq_begin + j) * H + h) * kHeadDim + 16 * cc;
+        const uint4 a = *reinterpret_cast<const uint4*>(src);
+        const uint4 b = *reinterpret_cast<const uint4*>(src + 8);
+        if (MODE == kObserve) mv = absmax8(absmax8(mv, a), b);
 #pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int row = it * 32 + (tid >> 3);
-    const int chunk = tid & 7;
-    const int pchunk = chunk ^ ((row >> 4) & 7);
-    const uint4 d = *reinterpret_cast<const uint4*>(&tile[row * kLdsRow + 16 * pchunk]);
-    *reinterpret_cast<uint4*>(v8t + ((int64_t)h * kHeadDim + row) * Tp + col0 + 16 * chunk) = d;
+        for (int c = 0; c < 8; ++c) {
+          x[r][c] = clamp_e4m3(bf16_at(a, c) * inv_v);
+          x[r][8 + c] = clamp_e4m3(bf16_at(b, c) * inv_v);
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < 16; ++c) x[r][c] = 0.0f;
+      }
+    }
+    // Transpose through LDS: row = channel, one dword = 4 keys of one channel. The dword
+    // column is XORed with 4 * (row / 16) so that the 8 channel chunks of a wave land in
+    // different banks; 16-byte chunks stay contiguous (chunk' = chunk ^ (row / 16)).
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+      int w = cvt_pk_e4m3<false>(x[0][c], x[1][c], 0);
+      w = cvt_pk_e4m3<true>(x[2][c], x[3][c], w);
+      const int row = 16 * cc + c;
+      *reinterpret_cast<int*>(&tile[row * kLdsRow + 4 * (kg ^ (4 * cc))]) = w;
+    }
+    __syncthreads();
+    // write 128 rows x 128 bytes: 8 threads per row, 16 bytes each, 4 rows per thread
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int row = it * 32 + (tid >> 3);
+      const int chunk = tid & 7;
+      const int pchunk = chunk ^ ((row >> 4) & 7);
+      const uint4 d = *reinterpret_cast<const uint4*>(&tile[row * kLdsRow + 16 * pchunk]);
+      *reinterpret_cast<uint4*>(v8t + ((int64_t)h * kHeadDim + row) * Tp + col0 + 16 * chunk) = d;
+    }
+    __syncthreads();                      // the tile buffer is rewritten by the next pair
   }
+  if (MODE == kObserve) publish_max(st, 2, mv, red);
+}
+
+template <int MODE>
+hipError_t launch_mode(fp8attn_state* st, const uint16_t* q, const uint16_t* k,
+                       const uint16_t* v, const int32_t* cu, int num_seqs, int64_t T, int H,
+                       uint8_t* q8, uint8_t* k8, uint8_t* v8t, int64_t Tp, hipStream_t s) {
+  const int64_t n = T * H * kHeadDim;
+  const int64_t per_block = (int64_t)kThreads * kQkGroups * 8;
+  int64_t nb_qk = (2 * n + per_block - 1) / per_block;
+  const int64_t cap = MODE == kRedo ? kMaxRedoBlocksPerPart : kMaxBlocksPerPart;
+  if (nb_qk > cap) nb_qk = cap;
+  int64_t nb_v = (Tp / kVTile) * H;
+  if (nb_v > cap) nb_v = cap;
+  if (nb_qk + nb_v <= 0) return hipSuccess;
+  hipLaunchKernelGGL(quantize_kernel<MODE>, dim3((unsigned)(nb_qk + nb_v)), dim3(kThreads), 0,
+                     s, st, q, k, v, cu, num_seqs, n, H, q8, k8, v8t, Tp, (int)nb_qk,
+                     (int)nb_v);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -128,15 +262,20 @@ hipError_t launch_quantize(const fp8attn_state* st, const uint16_t* q, const uin
                            const uint16_t* v, const int32_t* cu, int num_seqs, int64_t T,
                            int H, uint8_t* q8, uint8_t* k8, uint8_t* v8t, int64_t Tp,
                            hipStream_t s) {
-  const int64_t n = T * H * kHeadDim;
-  const int64_t nb_qk = (2 * n + kQkPerBlock - 1) / kQkPerBlock;
-  const int64_t nb_v = (Tp / kVTile) * H;
-  const int64_t blocks = nb_qk + nb_v;
-  if (blocks <= 0) return hipSuccess;
-  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, st, q, k,
-                     v, cu, num_seqs, n, H, q8, k8, v8t, Tp, (int)nb_qk);
-  return hipGetLastError();
+  // the plain mode only reads the state
+  return launch_mode<kPlain>(const_cast<fp8attn_state*>(st), q, k, v, cu, num_seqs, T, H, q8,
+                             k8, v8t, Tp, s);
+}
+
+hipError_t launch_quantize_dynamic(fp8attn_state* st, const uint16_t* q, const uint16_t* k,
+                                   const uint16_t* v, const int32_t* cu, int num_seqs,
+                                   int64_t T, int H, uint8_t* q8, uint8_t* k8, uint8_t* v8t,
+                                   int64_t Tp, hipStream_t s) {
+  hipError_t e = launch_mode<kObserve>(st, q, k, v, cu, num_seqs, T, H, q8, k8, v8t, Tp, s);
+  if (e != hipSuccess) return e;
+  e = launch_scales(st, FP8ATTN_DYNAMIC, nullptr, 0.0f, s);
+  if (e != hipSuccess) return e;
+  return launch_mode<kRedo>(st, q, k, v, cu, num_seqs, T, H, q8, k8, v8t, Tp, s);
 }
 
 }  // namespace fp8attn

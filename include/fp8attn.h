@@ -61,7 +61,10 @@ typedef enum fp8attn_status {
 #define FP8ATTN_STATIC 1  /* scale from a calibrated amax times a margin */
 
 /* Flags of fp8attn_forward. */
-#define FP8ATTN_SKIP 1u /* run the BF16 kernel on the unquantised inputs; state is not read */
+#define FP8ATTN_SKIP 1u    /* run the BF16 kernel on the unquantised inputs; state is not read */
+#define FP8ATTN_OBSERVE 2u /* dynamic scaling inside the call: the FP8 path quantises with
+                              fp8attn_quantize_dynamic (observe + ring + scales + quantise)
+                              instead of the state's current scales; excludes SKIP */
 
 #define FP8ATTN_RING_SLOTS 16
 /* Keys per online-softmax block of the FP8 path: P is quantised to E4M3 relative to the
@@ -160,6 +163,25 @@ int fp8attn_quantize(const void* state, const void* q, const void* k, const void
                      void* stream);
 
 /*
+ * One dynamic forward's scaling and quantisation in one call (vLLM docs "FP8 ViT Encoder
+ * Attention", "Usage": every dynamic forward observes the Q/K/V amax and the 16-slot ring
+ * drives its scale). The result -- state (ring, count, amax, scales) and workspace bytes --
+ * is exactly that of fp8attn_observe_amax, fp8attn_scales(FP8ATTN_DYNAMIC) and
+ * fp8attn_quantize in sequence. The work differs: the window maximum of this forward is
+ * max(A_pred, amax) with A_pred the maximum of the 15 ring slots that stay, so Q, K and V
+ * are quantised with A_pred's scale while their amax is observed in the same pass; after
+ * the scales update, only a tensor whose window maximum moved (its amax is a new maximum,
+ * e.g. on the first forward) is quantised again. In steady state Q, K and V are read once.
+ * The state's pending observation (cur) must be clear, as every fp8attn_scales call and
+ * fp8attn_state_reset leave it. Arguments as fp8attn_quantize; the state is written.
+ * Errors: as fp8attn_quantize.
+ */
+int fp8attn_quantize_dynamic(void* state, const void* q, const void* k, const void* v,
+                             const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+                             int num_seqs, int num_heads, int head_dim, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/*
  * FP8 attention on a workspace already filled by fp8attn_quantize with this state's
  * scales (the second half of the FP8 path of fp8attn_forward, which is exactly
  * fp8attn_quantize followed by fp8attn_attend). Arguments and the computation are those of
@@ -183,19 +205,23 @@ int fp8attn_attend(const void* state, const int32_t* cu_seqlens, const int32_t* 
  *   scale 448, so p8_j <= 448); earlier sums are rescaled by exp(m_old - m) when m grows;
  *   O = scale_v * sum_j p8'_j v8_j / sum_j p8'_j with p8' the rescaled weights. The PV
  *   product uses the E4M3 V; accumulation and softmax are fp32; O is bf16.
- *   Requires a preceding fp8attn_scales on this state (same stream).
+ *   Requires a preceding fp8attn_scales on this state (same stream), unless
+ *   FP8ATTN_OBSERVE is set: then the call itself performs the dynamic observe + ring +
+ *   scales update (fp8attn_quantize_dynamic) before the attention, writing the state.
  * BF16 path (FP8ATTN_SKIP): w_j = softmax(q.k_j * softmax_scale) in fp32 with P rounded
  *   to bf16 for the PV product; workspace and state are not used (may be NULL).
  * softmax_scale <= 0 selects 1/sqrt(head_dim).
  * cu_seqlens (device) and cu_seqlens_host (host) must hold the same values; the host
  * copy is used for checks and launch sizes so that no device read-back is needed.
- * Errors: EINVAL for NULL pointers, num_seqs < 1, num_heads < 1, total tokens beyond
+ * An empty batch (cu_seqlens_host[num_seqs] == 0) reads and writes no tensor element; q, k,
+ * v and out may then be NULL (with FP8ATTN_OBSERVE the ring still records a 0 observation).
+ * Errors: EINVAL for NULL pointers (other than those just named), num_seqs < 1, num_heads < 1, total tokens beyond
  * 2^31-1 elements per head row, a host cu_seqlens that does not start at 0 or decreases,
- * a workspace smaller than fp8attn_workspace_bytes, unknown flag bits, or a NULL state on
- * the FP8 path; EUNSUPPORTED for head_dim != 128, or when the longest sequence times
+ * a workspace smaller than fp8attn_workspace_bytes, unknown flag bits, SKIP together with
+ * OBSERVE, or a NULL state on the FP8 path; EUNSUPPORTED for head_dim != 128, or when the longest sequence times
  * num_heads * head_dim, or head_dim times the padded key count, reaches 2^31.
  */
-int fp8attn_forward(const void* state, const void* q, const void* k, const void* v,
+int fp8attn_forward(void* state, const void* q, const void* k, const void* v,
                     const int32_t* cu_seqlens, const int32_t* cu_seqlens_host, int num_seqs,
                     int num_heads, int head_dim, float softmax_scale, unsigned flags,
                     void* workspace, size_t workspace_bytes, void* out, void* stream);

@@ -33,7 +33,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 10, names
     for name in names:
         assert hasattr(lib, name), name
         assert name in _lib.SIGNATURES, name
@@ -75,7 +75,8 @@ def _fwd(lib, **kw):
     (dict(D=64), -2, "head_dim"),
     (dict(cu_host=_cu([1, 8, 16])), -1, "cu_seqlens[0]"),
     (dict(cu_host=_cu([0, 8, 4])), -1, "decreases"),
-    (dict(flags=2), -1, "flag"),
+    (dict(flags=4), -1, "flag"),
+    (dict(flags=3), -1, "exclude each other"),
     (dict(ws_bytes=100), -1, "workspace"),
     (dict(ws=NULL), -1, "workspace"),
     (dict(state=NULL), -1, "state"),
@@ -122,6 +123,23 @@ def test_scales_and_observe_reject(lib):
     assert lib.fp8attn_observe_amax(P, NULL, P, P, 128, NULL) == -1
     assert lib.fp8attn_observe_amax(P, ctypes.c_void_p(0x10002), P, P, 128, NULL) == -1
     assert lib.fp8attn_state_reset(NULL, NULL) == -1
+
+
+def test_quantize_dynamic_rejects(lib):
+    rc = lib.fp8attn_quantize_dynamic(NULL, P, P, P, P, _cu([0, 4]), 1, 1, 128, P2, 1 << 20, NULL)
+    assert rc == -1 and "state" in lib.fp8attn_last_error().decode()
+    rc = lib.fp8attn_quantize_dynamic(P, P, P, P, P, _cu([0, 4]), 1, 1, 128, P2, 10, NULL)
+    assert rc == -1 and "workspace" in lib.fp8attn_last_error().decode()
+    rc = lib.fp8attn_quantize_dynamic(P, P, P, P, P, _cu([0, 4]), 1, 1, 96, P2, 1 << 20, NULL)
+    assert rc == -2 and "head_dim" in lib.fp8attn_last_error().decode()
+
+
+def test_flag_constants_agree():
+    import fp8_dynamic_scaled_amd._lib as L
+    hdr = open(HEADER).read()
+    for name in ("FP8ATTN_SKIP", "FP8ATTN_OBSERVE", "FP8ATTN_DYNAMIC", "FP8ATTN_STATIC"):
+        m = re.search(rf"#define {name} (\d+)u?", hdr)
+        assert m and int(m.group(1)) == getattr(L, name), name
 
 
 def test_attend_rejects(lib):
