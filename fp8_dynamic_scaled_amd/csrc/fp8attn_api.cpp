@@ -265,6 +265,10 @@ int fp8attn_forward(void* state, const void* q, const void* k, const void* v,
   if (!std::isfinite(softmax_scale))
     return fail(FP8ATTN_EINVAL, "%s: softmax_scale must be finite", fn);
   const bool skip = (flags & FP8ATTN_SKIP) != 0;
+  // the BF16 kernel addresses one sequence of a bf16 tensor with 32-bit byte offsets
+  if (skip && (int64_t)vl.max_seqlen * num_heads * head_dim * 2 > ((int64_t)1 << 31) - 1)
+    return fail(FP8ATTN_EUNSUPPORTED,
+                "%s: the BF16 path needs longest sequence x num_heads x head_dim x 2 bytes < 2^31", fn);
   if (!skip) {
     if (!state) return fail(FP8ATTN_EINVAL, "%s: the FP8 path needs a state", fn);
     if (!workspace || !aligned16(workspace))

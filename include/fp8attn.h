@@ -219,7 +219,8 @@ int fp8attn_attend(const void* state, const int32_t* cu_seqlens, const int32_t* 
  * 2^31-1 elements per head row, a host cu_seqlens that does not start at 0 or decreases,
  * a workspace smaller than fp8attn_workspace_bytes, unknown flag bits, SKIP together with
  * OBSERVE, or a NULL state on the FP8 path; EUNSUPPORTED for head_dim != 128, or when the longest sequence times
- * num_heads * head_dim, or head_dim times the padded key count, reaches 2^31.
+ * num_heads * head_dim, or head_dim times the padded key count, reaches 2^31 (on the BF16
+ * path, when twice the former does).
  */
 int fp8attn_forward(void* state, const void* q, const void* k, const void* v,
                     const int32_t* cu_seqlens, const int32_t* cu_seqlens_host, int num_seqs,

@@ -95,6 +95,13 @@ def test_forward_rejects(lib, kw, code, needle):
     assert needle in lib.fp8attn_last_error().decode()
 
 
+def test_skip_path_rejects_sequences_beyond_32bit_byte_offsets(lib):
+    # 2^19 tokens x 16 heads x 128 channels x 2 bytes = 2^31: fine for FP8, not for BF16
+    cu = _cu([0, 1 << 19])
+    assert _fwd(lib, state=NULL, ws=NULL, ws_bytes=0, flags=1, cu_host=cu, num_seqs=1, H=16) == -2
+    assert "BF16" in lib.fp8attn_last_error().decode()
+
+
 def test_skip_path_needs_no_state_or_workspace_but_checks_the_rest(lib):
     # on the skip path a NULL state/workspace is fine; a bad head_dim still fails first
     assert _fwd(lib, state=NULL, ws=NULL, ws_bytes=0, flags=1, D=96) == -2
