@@ -20,7 +20,8 @@ DEFAULT_MARGIN = 1.5
 KV_BLOCK = 64          # FP8ATTN_KV_BLOCK: keys per online-softmax block of the FP8 path
 STATE_DTYPE = np.dtype([("ring", "<f4", (3, 16)), ("cur", "<u4", (3,)), ("count", "<u4"),
                         ("scale", "<f4", (3,)), ("inv_scale", "<f4", (3,)),
-                        ("amax", "<f4", (3,)), ("reserved", "<u4", (3,))])
+                        ("amax", "<f4", (3,)), ("moved", "<u4"),
+                        ("reserved", "<u4", (2,))])
 
 
 def _stream(device) -> ctypes.c_void_p:

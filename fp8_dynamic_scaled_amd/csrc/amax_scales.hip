@@ -9,7 +9,8 @@
 // block and tensor folds it into state->cur[t] as the fp32 bit image (non-negative
 // floats order like their bits).
 // scales_kernel: one wave; moves cur[t] into ring slot count mod 16, takes the window
-// maximum and writes scale = A/448, inv = 448/A (IEEE division), clears cur[t].
+// maximum and writes scale = A/448, inv = 448/A (IEEE division), clears cur[t], and records
+// in `moved` which tensors' window maximum this observation raised.
 #include "device_common.h"
 #include "launch.h"
 
@@ -91,13 +92,20 @@ __global__ void scales_kernel(fp8attn_state* st, int mode, float s0, float s1, f
                               float margin) {
   const int t = threadIdx.x;
   uint32_t count = st->count;
+  bool moved = false;
   if (t < 3) {
     float A;
     if (mode == FP8ATTN_DYNAMIC) {
-      st->ring[t][count % FP8ATTN_RING_SLOTS] = __uint_as_float(st->cur[t]);
-      A = 0.0f;
+      const uint32_t slot = count % FP8ATTN_RING_SLOTS;
+      // window maximum of the slots that stay, then with this forward's observation
+      float rest = 0.0f;
 #pragma unroll
-      for (int s = 0; s < FP8ATTN_RING_SLOTS; ++s) A = __builtin_fmaxf(A, st->ring[t][s]);
+      for (int s = 0; s < FP8ATTN_RING_SLOTS; ++s)
+        rest = __builtin_fmaxf(rest, (uint32_t)s == slot ? 0.0f : st->ring[t][s]);
+      const float obs = __uint_as_float(st->cur[t]);
+      st->ring[t][slot] = obs;
+      A = __builtin_fmaxf(rest, obs);
+      moved = A != rest;
     } else {
       const float cal = t == 0 ? s0 : (t == 1 ? s1 : s2);
       A = cal * margin;
@@ -107,8 +115,12 @@ __global__ void scales_kernel(fp8attn_state* st, int mode, float s0, float s1, f
     st->inv_scale[t] = inv_scale_from_amax(A);
     st->cur[t] = 0u;
   }
+  const uint32_t mask = (uint32_t)(__builtin_amdgcn_ballot_w64(moved) & 7u);
   __syncthreads();
-  if (t == 0 && mode == FP8ATTN_DYNAMIC) st->count = count + 1;
+  if (t == 0) {
+    st->moved = mask;
+    if (mode == FP8ATTN_DYNAMIC) st->count = count + 1;
+  }
 }
 
 __global__ void state_reset_kernel(uint32_t* words, int nwords) {

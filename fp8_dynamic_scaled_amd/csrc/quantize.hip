@@ -21,9 +21,9 @@
 //    observation replaces. The kernel quantises with A_pred's scale and, in the same pass
 //    over the input, observes amax into the state's pending slot (as the amax kernel
 //    does). The scales kernel then runs as usual.
-//  * kRedo (after the scales kernel): recomputes A_pred from the ring (every slot but the
-//    one just written) and re-quantises a tensor only when its final A differs, i.e. when
-//    this forward's amax is a new window maximum; otherwise its blocks return at once.
+//  * kRedo (after the scales kernel): re-quantises a tensor only when the scales kernel
+//    recorded that its window maximum moved (this forward's amax exceeded A_pred);
+//    otherwise its blocks return after one load.
 // The bytes are therefore exactly those of amax + scales + plain quantise, while in steady
 // state Q, K and V are read once instead of twice.
 #include "device_common.h"
@@ -38,10 +38,6 @@ constexpr int kQkGroups = 4;                                    // 8-element gro
 constexpr int kVTile = 128;                                     // keys per V tile
 constexpr int kLdsRow = kVTile + 16;                            // bytes per LDS row (16B aligned)
 constexpr int kMaxBlocksPerPart = 1024;                         // Q/K blocks, V blocks
-// The re-quantise pass usually has nothing to do and its blocks return at once, so its
-// grid is kept small (its cost is then mostly the launch); when it does work -- the first
-// forward of a layer, or a new window maximum -- the grid-stride loops cover everything.
-constexpr int kMaxRedoBlocksPerPart = 128;
 
 enum QuantMode { kPlain = 0, kObserve = 1, kRedo = 2 };
 
@@ -72,12 +68,16 @@ __device__ __forceinline__ uint32_t absmax8(uint32_t m, const uint4& r) {
 }
 
 // Largest ring entry of tensor t other than slot `skip`: the window maximum that this
-// forward's observation (in slot `skip`) can only raise.
+// forward's observation (in slot `skip`) can only raise. Every slot is loaded and the
+// skipped one counts as 0 (entries are >= 0): a conditional load per slot would become a
+// chain of dependent scalar loads.
 __device__ __forceinline__ float ring_max_except(const fp8attn_state* st, int t, uint32_t skip) {
+  float r[FP8ATTN_RING_SLOTS];
+#pragma unroll
+  for (int s = 0; s < FP8ATTN_RING_SLOTS; ++s) r[s] = st->ring[t][s];
   float a = 0.0f;
 #pragma unroll
-  for (int s = 0; s < FP8ATTN_RING_SLOTS; ++s)
-    if ((uint32_t)s != skip) a = __builtin_fmaxf(a, st->ring[t][s]);
+  for (int s = 0; s < FP8ATTN_RING_SLOTS; ++s) a = __builtin_fmaxf(a, (uint32_t)s == skip ? 0.0f : r[s]);
   return a;
 }
 
@@ -125,9 +125,9 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
 #pragma unroll
     for (int t = 0; t < 3; ++t) inv[t] = st->inv_scale[t];
     if (MODE == kRedo) {
-      const uint32_t slot = (st->count - 1u) % FP8ATTN_RING_SLOTS;   // just written
+      const uint32_t moved = st->moved;             // written by the scales kernel
 #pragma unroll
-      for (int t = 0; t < 3; ++t) work[t] = st->amax[t] != ring_max_except(st, t, slot);
+      for (int t = 0; t < 3; ++t) work[t] = (moved >> t) & 1u;
     }
   }
 
@@ -245,7 +245,11 @@ hipError_t launch_mode(fp8attn_state* st, const uint16_t* q, const uint16_t* k,
   const int64_t n = T * H * kHeadDim;
   const int64_t per_block = (int64_t)kThreads * kQkGroups * 8;
   int64_t nb_qk = (2 * n + per_block - 1) / per_block;
-  const int64_t cap = MODE == kRedo ? kMaxRedoBlocksPerPart : kMaxBlocksPerPart;
+  // the re-quantise pass keeps the full grid: when it works (the first forward of a layer,
+  // or a new window maximum -- with amax varying between forwards, one of Q/K/V does so in
+  // several forwards of 16) it must run at full speed, and its blocks exit after one load
+  // when it does not
+  const int64_t cap = kMaxBlocksPerPart;
   if (nb_qk > cap) nb_qk = cap;
   int64_t nb_v = (Tp / kVTile) * H;
   if (nb_v > cap) nb_v = cap;

@@ -86,6 +86,9 @@ typedef enum fp8attn_status {
  *   scale[t]     dequantisation scale A/448 of the current forward.
  *   inv_scale[t] quantisation multiplier 448/A of the current forward.
  *   amax[t]      the A behind scale[t] (window maximum, or static amax times margin).
+ *   moved        bit t set when the last dynamic scale update changed tensor t's window
+ *                maximum, i.e. its new observation exceeded the other 15 slots (0 after a
+ *                static update); fp8attn_quantize_dynamic re-quantises exactly those.
  */
 typedef struct fp8attn_state {
   float ring[3][FP8ATTN_RING_SLOTS];
@@ -94,7 +97,8 @@ typedef struct fp8attn_state {
   float scale[3];
   float inv_scale[3];
   float amax[3];
-  uint32_t reserved[3];
+  uint32_t moved;
+  uint32_t reserved[2];
 } fp8attn_state;
 
 /* Size in bytes of fp8attn_state (256). */

@@ -9,11 +9,15 @@ falling draws that push the old maximum out of the 16-slot window, an all-zero t
 an empty batch (only the ring moves). Correctness against the oracle follows from the
 separate path's own parity tests.
 """
+import numpy as np
 import pytest
 import torch
 
+import oracle
 import fp8_dynamic_scaled_amd as fa
 from workloads import random_varlen
+
+from parity_util import amax_exact
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -40,6 +44,7 @@ def test_one_pass_dynamic_equals_separate_calls():
     H = 2
     one = fa.AttentionLayer(DEV)                     # one_pass=True (the default)
     sep = fa.AttentionLayer(DEV, one_pass=False)
+    ring = oracle.AmaxRing()
     for f, (tag, seed, sq, sk, sv, lens) in enumerate(_schedule()):
         q, k, v, cu = random_varlen(lens, H, seed=seed, device=DEV, outliers=True)
         q = (q.float() * sq).to(torch.bfloat16)
@@ -51,6 +56,13 @@ def test_one_pass_dynamic_equals_separate_calls():
         torch.cuda.synchronize()
         s1, s2 = fa.read_state(one.state), fa.read_state(sep.state)
         assert torch.equal(one.state, sep.state), (f, tag, s1, s2)
+        # moved bit t: this forward's amax exceeds the 15 slots that stay (oracle ring)
+        amax = [amax_exact(x) if x.numel() else 0.0 for x in (q, k, v)]
+        slot = ring.count % oracle.RING_SLOTS
+        rest = [float(np.max(np.delete(ring.slots[t], slot))) for t in range(3)]
+        ring.update(amax)
+        want = sum(1 << t for t in range(3) if amax[t] > rest[t])
+        assert int(s1["moved"]) == want, (f, tag, int(s1["moved"]), want)
         T = q.shape[0]
         if T:
             B = len(cu) - 1
