@@ -19,7 +19,7 @@ Infinity Cache: on the same batch with a 512 MB device write before every launch
 write evicts the cache), and on the 3-image 4K batch (3 x 32400 tokens, 16 heads, 1.2 GB
 of bf16 input), each timed over back-to-back steps of amax + scales + quantise.
 
---gpus N > 1 is refused: this build runs on one GPU.
+--gpus N > 1 is refused: the benchmark runs on one GPU.
 """
 import argparse
 import hashlib
@@ -196,7 +196,7 @@ def cold_quant(fa, w, q, k, v, cu_d, cu, st, ws, dev, reps=10):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+        print(json.dumps({"error": "the benchmark runs on one GPU; --gpus must be 1",
                           "n_gpus_requested": args.gpus}))
         sys.exit(2)
 

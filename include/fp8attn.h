@@ -52,7 +52,7 @@ extern "C" {
 typedef enum fp8attn_status {
   FP8ATTN_OK = 0,
   FP8ATTN_EINVAL = -1,      /* a null pointer, a size out of range, inconsistent cu_seqlens */
-  FP8ATTN_EUNSUPPORTED = -2, /* a valid request this build does not implement (head_dim != 128) */
+  FP8ATTN_EUNSUPPORTED = -2, /* a valid request the library does not implement (head_dim != 128) */
   FP8ATTN_EHIP = -3          /* the HIP runtime reported an error while enqueuing */
 } fp8attn_status;
 
