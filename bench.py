@@ -52,6 +52,8 @@ def parse():
                     help="query rows per head in the oracle's timed attention sample")
     ap.add_argument("--no-cold-quant", action="store_true",
                     help="skip the quantisation measurements beyond the Infinity Cache")
+    ap.add_argument("--no-regime", action="store_true",
+                    help="skip the image-resolution sweep and the DiT-forward comparison")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the benchmark, run one plain device copy of this many MiB "
                          "(reference for HBM byte counters)")
@@ -193,6 +195,74 @@ def cold_quant(fa, w, q, k, v, cu_d, cu, st, ws, dev, reps=10):
     return out
 
 
+# The end-to-end encoder table of the pages' FP8 ViT attention section ("Performance"):
+# 3 images per request at HD, FullHD, QHD and 4K. Patches of 16 pixels; the FullHD height
+# is taken as 1088 (68 patch rows), the next multiple of 32, so every image splits into
+# whole 2x2-merged patch groups. A 448x448 image (28x28 patches) is added below them.
+RESOLUTIONS = (("448x448", 28, 28), ("HD 720x1280", 45, 80), ("FullHD 1080x1920", 68, 120),
+               ("QHD 1440x2560", 90, 160), ("4K 2160x3840", 135, 240))
+
+
+def _median_ms(fn, reps):
+    import torch
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+    for e in ev:
+        e[0].record()
+        fn()
+        e[1].record()
+    torch.cuda.synchronize()
+    t = sorted(e[0].elapsed_time(e[1]) for e in ev)
+    return t[len(t) // 2]
+
+
+def regime(fa, dev, reps=7):
+    """FP8 dynamic step (one-pass quantise + FP8 attention) against the BF16 kernel on
+    3-image batches per resolution (16 heads, bf16 N(0,1) with x20 outlier columns), and on
+    one forward of the DiT video workload (57600 tokens, 40 heads)."""
+    import torch
+    from workloads import WORKLOADS, Workload, make_qkv
+    rows = {}
+    cases = [(name, Workload(name, 6, tuple(i * ph * pw for i in range(4)), 16, outliers=True))
+             for name, ph, pw in RESOLUTIONS]
+    cases.append(("DiT forward 57600 tokens, H=40", WORKLOADS["dit"]))
+    for name, w in cases:
+        q, k, v = make_qkv(w, 0, dev)
+        cu = list(w.cu_seqlens)
+        cu_d = torch.tensor(cu, dtype=torch.int32, device=dev)
+        H = w.num_heads
+        st = fa.new_state(dev)
+        ws = torch.empty(fa.workspace_bytes(w.total_tokens, w.num_seqs, H, w.head_dim),
+                         dtype=torch.uint8, device=dev)
+        out = torch.empty_like(q)
+
+        def quant():
+            fa.quantize_dynamic(st, q, k, v, cu_d, cu, workspace=ws)
+
+        def attn():
+            fa.attend(st, ws, cu_d, cu, H, out=out)
+
+        def fp8_step():
+            quant()
+            attn()
+
+        def bf16():
+            fa.forward(None, q, k, v, cu_d, cu, skip=True, out=out)
+
+        for _ in range(3):
+            fp8_step()
+            bf16()
+        t_step, t_q, t_a, t_b = (_median_ms(f, reps) for f in (fp8_step, quant, attn, bf16))
+        rows[name] = {"tokens_per_image": w.seq_lens[0], "images": w.num_seqs, "heads": H,
+                      "fp8_step_ms": round(t_step, 4), "quantize_dynamic_ms": round(t_q, 4),
+                      "attn_fp8_ms": round(t_a, 4), "attn_bf16_ms": round(t_b, 4),
+                      "fp8_step_speedup": round(t_b / t_step, 3),
+                      "attn_only_speedup": round(t_b / t_a, 3),
+                      "attn_fp8_tflops": round(w.flops() / (t_a * 1e-3) / 1e12, 1)}
+        del q, k, v, ws, out
+        torch.cuda.empty_cache()
+    return rows
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -327,6 +397,12 @@ def main():
     }
     if cold is not None:
         result["quant_beyond_infinity_cache"] = cold
+    if not args.no_regime:
+        result["resolution_sweep"] = regime(fa, dev)
+        result["resolution_sweep_note"] = (
+            "median of 7; fp8_step = fp8attn_quantize_dynamic + fp8attn_attend (dynamic "
+            "scaling, window maximum steady), attn_bf16 = the skip-path kernel; 3 images "
+            "per request, 16-pixel patches, H=16 (DiT: one forward, H=40)")
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, q, k, v, cu, args.cpu_rows)
     if args.copy_calibration_mib > 0:
