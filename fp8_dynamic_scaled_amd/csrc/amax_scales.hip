@@ -94,26 +94,19 @@ __global__ void scales_kernel(fp8attn_state* st, int mode, float s0, float s1, f
   uint32_t count = st->count;
   bool moved = false;
   if (t < 3) {
-    float A;
     if (mode == FP8ATTN_DYNAMIC) {
-      const uint32_t slot = count % FP8ATTN_RING_SLOTS;
       // window maximum of the slots that stay, then with this forward's observation
-      float rest = 0.0f;
-#pragma unroll
-      for (int s = 0; s < FP8ATTN_RING_SLOTS; ++s)
-        rest = __builtin_fmaxf(rest, (uint32_t)s == slot ? 0.0f : st->ring[t][s]);
-      const float obs = __uint_as_float(st->cur[t]);
-      st->ring[t][slot] = obs;
-      A = __builtin_fmaxf(rest, obs);
-      moved = A != rest;
+      const uint32_t slot = count % FP8ATTN_RING_SLOTS;
+      moved = dynamic_update(st, t, slot, ring_max_except(st, t, slot),
+                             __uint_as_float(st->cur[t]));
     } else {
       const float cal = t == 0 ? s0 : (t == 1 ? s1 : s2);
-      A = cal * margin;
+      const float A = cal * margin;
+      st->amax[t] = A;
+      st->scale[t] = scale_from_amax(A);
+      st->inv_scale[t] = inv_scale_from_amax(A);
+      st->cur[t] = 0u;
     }
-    st->amax[t] = A;
-    st->scale[t] = scale_from_amax(A);
-    st->inv_scale[t] = inv_scale_from_amax(A);
-    st->cur[t] = 0u;
   }
   const uint32_t mask = (uint32_t)(__builtin_amdgcn_ballot_w64(moved) & 7u);
   __syncthreads();

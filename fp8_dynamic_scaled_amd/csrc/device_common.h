@@ -43,6 +43,34 @@ __device__ __forceinline__ float inv_scale_from_amax(float A) {
   return kE4M3Max / __builtin_fmaxf(A, kAmaxFloor);
 }
 
+// Largest ring entry of tensor t other than slot `skip`: the window maximum that the
+// observation going into slot `skip` can only raise. Every slot is loaded and the skipped
+// one counts as 0 (entries are >= 0): a conditional load per slot would become a chain of
+// dependent scalar loads.
+__device__ __forceinline__ float ring_max_except(const fp8attn_state* st, int t, uint32_t skip) {
+  float r[FP8ATTN_RING_SLOTS];
+#pragma unroll
+  for (int s = 0; s < FP8ATTN_RING_SLOTS; ++s) r[s] = st->ring[t][s];
+  float a = 0.0f;
+#pragma unroll
+  for (int s = 0; s < FP8ATTN_RING_SLOTS; ++s) a = __builtin_fmaxf(a, (uint32_t)s == skip ? 0.0f : r[s]);
+  return a;
+}
+
+// One tensor's dynamic scale update: observation obs replaces ring slot `slot`, whose
+// other slots' maximum is rest. Writes the window maximum A = max(rest, obs) with its scale
+// pair, clears the pending observation, and returns whether A moved (A != rest).
+__device__ __forceinline__ bool dynamic_update(fp8attn_state* st, int t, uint32_t slot,
+                                               float rest, float obs) {
+  st->ring[t][slot] = obs;
+  const float A = __builtin_fmaxf(rest, obs);
+  st->amax[t] = A;
+  st->scale[t] = scale_from_amax(A);
+  st->inv_scale[t] = inv_scale_from_amax(A);
+  st->cur[t] = 0u;
+  return A != rest;
+}
+
 __device__ __forceinline__ float clamp_e4m3(float y) {
   return __builtin_fminf(__builtin_fmaxf(y, -kE4M3Max), kE4M3Max);
 }

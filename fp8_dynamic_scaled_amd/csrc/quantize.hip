@@ -67,20 +67,6 @@ __device__ __forceinline__ uint32_t absmax8(uint32_t m, const uint4& r) {
   return a.x > a.y ? a.x : a.y;
 }
 
-// Largest ring entry of tensor t other than slot `skip`: the window maximum that this
-// forward's observation (in slot `skip`) can only raise. Every slot is loaded and the
-// skipped one counts as 0 (entries are >= 0): a conditional load per slot would become a
-// chain of dependent scalar loads.
-__device__ __forceinline__ float ring_max_except(const fp8attn_state* st, int t, uint32_t skip) {
-  float r[FP8ATTN_RING_SLOTS];
-#pragma unroll
-  for (int s = 0; s < FP8ATTN_RING_SLOTS; ++s) r[s] = st->ring[t][s];
-  float a = 0.0f;
-#pragma unroll
-  for (int s = 0; s < FP8ATTN_RING_SLOTS; ++s) a = __builtin_fmaxf(a, (uint32_t)s == skip ? 0.0f : r[s]);
-  return a;
-}
-
 // Block-wide max of per-thread 16-bit magnitudes; thread 0 folds the result into the
 // pending observation state->cur[t] (fp32 bit image; a plain load first filters the blocks
 // that cannot raise it, since atomics on one address serialise in L2).
