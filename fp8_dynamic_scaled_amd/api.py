@@ -168,7 +168,7 @@ def split_workspace(workspace: torch.Tensor, total_tokens: int, num_seqs: int, n
                     head_dim: int = HEAD_DIM):
     """Views (q8 [T,H,D], k8 [T,H,D], v8t [H,D,Tp]) of a workspace (uint8)."""
     n = total_tokens * num_heads * head_dim
-    Tp = (total_tokens + 127) // 128 * 128 + 256 * num_seqs
+    Tp = (total_tokens + 127) // 128 * 128 + 128 * num_seqs
     q8 = workspace[:n].view(total_tokens, num_heads, head_dim)
     k8 = workspace[n:2 * n].view(total_tokens, num_heads, head_dim)
     v8t = workspace[2 * n:2 * n + num_heads * head_dim * Tp].view(num_heads, head_dim, Tp)
@@ -177,7 +177,7 @@ def split_workspace(workspace: torch.Tensor, total_tokens: int, num_seqs: int, n
 
 def pad_start(cu_i: int, i: int) -> int:
     """First padded key column of sequence i in V8t (see fp8attn.h)."""
-    return (cu_i + 127) // 128 * 128 + 256 * i
+    return (cu_i + 127) // 128 * 128 + 128 * i
 
 
 def attend(state, workspace, cu_seqlens, cu_seqlens_host, num_heads: int,

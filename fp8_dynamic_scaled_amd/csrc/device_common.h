@@ -94,7 +94,7 @@ __device__ __forceinline__ bool wave_any(bool p) {
 
 // Start column of sequence i in the key-contiguous V8t layout (see fp8attn.h).
 __device__ __host__ __forceinline__ int64_t pad_start(int64_t cu_i, int i) {
-  return ((cu_i + 127) / 128) * 128 + 256 * (int64_t)i;
+  return ((cu_i + 127) / 128) * 128 + 128 * (int64_t)i;
 }
 
 }  // namespace fp8attn

@@ -42,7 +42,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
-int64_t padded_keys(int64_t T, int num_seqs) { return round_up(T, 128) + 256 * (int64_t)num_seqs; }
+int64_t padded_keys(int64_t T, int num_seqs) { return round_up(T, 128) + 128 * (int64_t)num_seqs; }
 
 struct Varlen {
   int64_t T = 0;

@@ -8,10 +8,11 @@
 //
 // Work split (grid-stride, so the grid stays small whatever the batch): blocks
 // [0, nb_qk) stream Q and K element-wise into [T][H][D] (four 16-byte groups in flight
-// per thread); blocks [nb_qk, nb_qk + nb_v) walk (head, 128-column tile) pairs of the
-// padded key axis of V8t [H][D][Tp] (see fp8attn.h): each loads 128 tokens x 128
-// channels of V, quantises, transposes through LDS and writes 128 channel rows of 128
-// contiguous key bytes. Columns outside every sequence are written as 0 so the attention
+// per thread); blocks [nb_qk, nb_qk + nb_v) each take a contiguous run of (128-column
+// tile, head) pairs of the padded key axis of V8t [H][D][Tp] (see fp8attn.h), so the
+// sequence that holds a tile is found once per run and then stepped; each pair loads 128
+// tokens x 128 channels of V, quantises, transposes through LDS and writes 128 channel
+// rows of 128 contiguous key bytes. Columns outside every sequence are written as 0 so the attention
 // kernel can read whole tiles without bounds checks on V.
 //
 // Three modes share that kernel:
@@ -158,23 +159,33 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
     return;
   }
 
-  // ---- V: (padded key tile, head) pairs, grid-stride
+  // ---- V: (padded key tile, head) pairs; each block takes a contiguous run of them, in
+  // which the key tile -- and so the sequence -- only moves forward
   if (MODE == kRedo && !work[2]) return;
   const float inv_v = inv[2];
   const int64_t tiles = (Tp / kVTile) * H;
+  const int64_t run = (tiles + nb_v - 1) / nb_v;
+  const int64_t vb_begin = ((int64_t)blockIdx.x - nb_qk) * run;
+  const int64_t vb_end = vb_begin + run < tiles ? vb_begin + run : tiles;
   const int cc = tid & 7;           // channel chunk: channels 16cc .. 16cc+15
   const int kg = tid >> 3;          // key group: keys 4kg .. 4kg+3 of the tile
   uint32_t mv = 0;
-  for (int64_t vb = (int64_t)blockIdx.x - nb_qk; vb < tiles; vb += nb_v) {
+  int seq = -1;
+  for (int64_t vb = vb_begin; vb < vb_end; ++vb) {
     const int h = (int)(vb % H);
     const int64_t col0 = (vb / H) * kVTile;          // first padded key column of the tile
-    // sequence whose padded region holds col0: largest i with pad_start(i) <= col0
-    int lo = 0, hi = num_seqs - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (pad_start(cu[mid], mid) <= col0) lo = mid; else hi = mid - 1;
+    // sequence whose padded region holds col0: the largest i with pad_start(i) <= col0
+    // (starts increase strictly); a binary search for the run's first tile, then steps
+    if (seq < 0) {
+      int lo = 0, hi = num_seqs - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (pad_start(cu[mid], mid) <= col0) lo = mid; else hi = mid - 1;
+      }
+      seq = lo;
+    } else {
+      while (seq + 1 < num_seqs && pad_start(cu[seq + 1], seq + 1) <= col0) ++seq;
     }
-    const int seq = lo;
     const int64_t seq_begin = cu[seq];
     const int64_t seq_len = (int64_t)cu[seq + 1] - seq_begin;
     const int64_t j0 = col0 - pad_start(seq_begin, seq);  // key offset inside the sequence

@@ -146,8 +146,10 @@ int fp8attn_scales(void* state, int mode, const float* static_amax_host, float m
  *   K8 e4m3 [T][H][D] at offset T*H*D,
  *   V8t e4m3 [H][D][Tp] at offset 2*T*H*D: V transposed so that keys are contiguous,
  *     where sequence i occupies columns [pad_start(i), pad_start(i) + S_i) with
- *     pad_start(i) = roundup(cu[i], 128) + 256*i, and every other column is 0;
- *     Tp = roundup(T, 128) + 256*num_seqs.
+ *     pad_start(i) = roundup(cu[i], 128) + 128*i, and every other column is 0;
+ *     Tp = roundup(T, 128) + 128*num_seqs. (Every start is 128-aligned and lies past the
+ *     previous sequence's last column, so whole 64-key tiles read past a sequence's end
+ *     see zeros, and each 128-column tile belongs to one sequence.)
  * Returns 0 for negative or overflowing arguments.
  */
 size_t fp8attn_workspace_bytes(int64_t total_tokens, int num_seqs, int num_heads,

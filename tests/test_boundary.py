@@ -45,7 +45,7 @@ def test_sizes(lib):
     from fp8_dynamic_scaled_amd.api import STATE_DTYPE
     assert STATE_DTYPE.itemsize == 256
     T, B, H, D = 43200, 3, 16, 128
-    Tp = (T + 127) // 128 * 128 + 256 * B
+    Tp = (T + 127) // 128 * 128 + 128 * B
     assert lib.fp8attn_workspace_bytes(T, B, H, D) == 2 * T * H * D + H * D * Tp
     assert lib.fp8attn_workspace_bytes(-1, 1, 16, 128) == 0
     assert lib.fp8attn_workspace_bytes(10, 0, 16, 128) == 0
@@ -175,12 +175,13 @@ def test_pad_start_regions_hold_their_sequences():
         lens = rng.integers(0, 400, size=rng.integers(1, 8))
         cu = np.concatenate([[0], np.cumsum(lens)])
         starts = [fa.pad_start(int(cu[i]), i) for i in range(len(lens) + 1)]
-        Tp = (int(cu[-1]) + 127) // 128 * 128 + 256 * len(lens)
+        Tp = (int(cu[-1]) + 127) // 128 * 128 + 128 * len(lens)
         assert starts[-1] == Tp
         for i, s in enumerate(lens):
             assert starts[i] % 128 == 0
-            # room for the sequence plus a zero tail covering a whole 64/128-key tile
-            assert starts[i + 1] - starts[i] >= s + 129
+            # the next sequence starts at or past the end of the last whole 128-column tile
+            # that holds this one: tiles of 64 or 128 keys read past its end see only zeros
+            assert starts[i + 1] - starts[i] >= (int(s) + 127) // 128 * 128
 
 
 def test_kv_block_constant_agrees():
