@@ -198,9 +198,13 @@ def cold_quant(fa, w, q, k, v, cu_d, cu, st, ws, dev, reps=10):
 # The end-to-end encoder table of the pages' FP8 ViT attention section ("Performance"):
 # 3 images per request at HD, FullHD, QHD and 4K. Patches of 16 pixels; the FullHD height
 # is taken as 1088 (68 patch rows), the next multiple of 32, so every image splits into
-# whole 2x2-merged patch groups. A 448x448 image (28x28 patches) is added below them.
-RESOLUTIONS = (("448x448", 28, 28), ("HD 720x1280", 45, 80), ("FullHD 1080x1920", 68, 120),
-               ("QHD 1440x2560", 90, 160), ("4K 2160x3840", 135, 240))
+# whole 2x2-merged patch groups. A 448x448 image (28x28 patches) is added below them, and
+# two batches of many small images.
+RESOLUTIONS = (("448x448", 28, 28, 3), ("HD 720x1280", 45, 80, 3),
+               ("FullHD 1080x1920", 68, 120, 3), ("QHD 1440x2560", 90, 160, 3),
+               ("4K 2160x3840", 135, 240, 3),
+               # many small images in one batch: the short-sequence regime
+               ("448x448 x64", 28, 28, 64), ("256x256 x256", 16, 16, 256))
 
 
 def _median_ms(fn, reps):
@@ -222,8 +226,9 @@ def regime(fa, dev, reps=7):
     import torch
     from workloads import WORKLOADS, Workload, make_qkv
     rows = {}
-    cases = [(name, Workload(name, 6, tuple(i * ph * pw for i in range(4)), 16, outliers=True))
-             for name, ph, pw in RESOLUTIONS]
+    cases = [(name, Workload(name, 6, tuple(i * ph * pw for i in range(n + 1)), 16,
+                             outliers=True))
+             for name, ph, pw, n in RESOLUTIONS]
     cases.append(("DiT forward 57600 tokens, H=40", WORKLOADS["dit"]))
     for name, w in cases:
         q, k, v = make_qkv(w, 0, dev)
@@ -402,7 +407,8 @@ def main():
         result["resolution_sweep_note"] = (
             "median of 7; fp8_step = fp8attn_quantize_dynamic + fp8attn_attend (dynamic "
             "scaling, window maximum steady), attn_bf16 = the skip-path kernel; 3 images "
-            "per request, 16-pixel patches, H=16 (DiT: one forward, H=40)")
+            "per request unless the name says x N, 16-pixel patches, H=16 (DiT: one "
+            "forward, H=40)")
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, q, k, v, cu, args.cpu_rows)
     if args.copy_calibration_mib > 0:
