@@ -18,10 +18,11 @@ from ._lib import FP8ATTN_DYNAMIC, FP8ATTN_OBSERVE, FP8ATTN_SKIP, FP8ATTN_STATIC
 HEAD_DIM = 128
 DEFAULT_MARGIN = 1.5
 KV_BLOCK = 64          # FP8ATTN_KV_BLOCK: keys per online-softmax block of the FP8 path
-STATE_DTYPE = np.dtype([("ring", "<f4", (3, 16)), ("cur", "<u4", (3,)), ("count", "<u4"),
+CUR_STRIPES = 16       # FP8ATTN_CUR_STRIPES
+STATE_DTYPE = np.dtype([("ring", "<f4", (3, 16)), ("count", "<u4"),
                         ("scale", "<f4", (3,)), ("inv_scale", "<f4", (3,)),
-                        ("amax", "<f4", (3,)), ("moved", "<u4"),
-                        ("reserved", "<u4", (2,))])
+                        ("amax", "<f4", (3,)), ("moved", "<u4"), ("reserved", "<u4", (5,)),
+                        ("cur", "<u4", (CUR_STRIPES, 16))])
 
 
 def _stream(device) -> ctypes.c_void_p:
@@ -69,7 +70,7 @@ def state_reset(state: torch.Tensor) -> None:
 
 
 def new_state(device=None) -> torch.Tensor:
-    """A zeroed per-layer state (256 bytes of device memory)."""
+    """A zeroed per-layer state (fp8attn_state_bytes() = 1280 bytes of device memory)."""
     device = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
     st = torch.empty(state_bytes(), dtype=torch.uint8, device=device)
     state_reset(st)

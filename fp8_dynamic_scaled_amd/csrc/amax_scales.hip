@@ -5,11 +5,12 @@
 //
 // amax_kernel: one launch reads Q, K and V (bf16) once; HBM-bound. Each thread keeps a
 // packed 16-bit max of |x| (the bf16 bit pattern with the sign cleared orders like the
-// magnitude), the block reduces through a wave shuffle and LDS, and one atomicMax per
-// block and tensor folds it into state->cur[t] as the fp32 bit image (non-negative
-// floats order like their bits).
-// scales_kernel: one wave; moves cur[t] into ring slot count mod 16, takes the window
-// maximum and writes scale = A/448, inv = 448/A (IEEE division), clears cur[t], and records
+// magnitude), the block reduces through a wave shuffle and LDS, and at most one atomicMax
+// per block and tensor folds it into the block's stripe of state->cur as the fp32 bit image
+// (non-negative floats order like their bits).
+// scales_kernel: one wave; gathers tensor t's observation from its stripes into ring slot
+// count mod 16, takes the window maximum and writes scale = A/448, inv = 448/A (IEEE
+// division), clears the stripes, and records
 // in `moved` which tensors' window maximum this observation raised.
 #include "device_common.h"
 #include "launch.h"
@@ -79,12 +80,9 @@ __global__ __launch_bounds__(kAmaxThreads) void amax_kernel(fp8attn_state* st,
     uint32_t b = red[0];
 #pragma unroll
     for (int w = 1; w < kAmaxThreads / 64; ++w) b = red[w] > b ? red[w] : b;
-    // bf16 magnitude -> fp32 bit image, then fold into the pending observation; a plain
-    // load first filters the blocks that cannot raise it (atomics on one address
-    // serialise in L2)
-    const uint32_t img = b << 16;
-    if (img != 0 && img > __hip_atomic_load(&st->cur[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
-      atomicMax(&st->cur[t], img);
+    // bf16 magnitude -> fp32 bit image, then fold into this block's stripe of the pending
+    // observation
+    fold_max(&st->cur[blockIdx.x % FP8ATTN_CUR_STRIPES][t], b << 16);
   }
 }
 
@@ -98,14 +96,14 @@ __global__ void scales_kernel(fp8attn_state* st, int mode, float s0, float s1, f
       // window maximum of the slots that stay, then with this forward's observation
       const uint32_t slot = count % FP8ATTN_RING_SLOTS;
       moved = dynamic_update(st, t, slot, ring_max_except(st, t, slot),
-                             __uint_as_float(st->cur[t]));
+                             take_observation(st, t));
     } else {
       const float cal = t == 0 ? s0 : (t == 1 ? s1 : s2);
       const float A = cal * margin;
       st->amax[t] = A;
       st->scale[t] = scale_from_amax(A);
       st->inv_scale[t] = inv_scale_from_amax(A);
-      st->cur[t] = 0u;
+      take_observation(st, t);   // cleared; a static update does not use it
     }
   }
   const uint32_t mask = (uint32_t)(__builtin_amdgcn_ballot_w64(moved) & 7u);

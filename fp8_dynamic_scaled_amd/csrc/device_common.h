@@ -59,7 +59,7 @@ __device__ __forceinline__ float ring_max_except(const fp8attn_state* st, int t,
 
 // One tensor's dynamic scale update: observation obs replaces ring slot `slot`, whose
 // other slots' maximum is rest. Writes the window maximum A = max(rest, obs) with its scale
-// pair, clears the pending observation, and returns whether A moved (A != rest).
+// pair and returns whether A moved (A != rest).
 __device__ __forceinline__ bool dynamic_update(fp8attn_state* st, int t, uint32_t slot,
                                                float rest, float obs) {
   st->ring[t][slot] = obs;
@@ -67,8 +67,31 @@ __device__ __forceinline__ bool dynamic_update(fp8attn_state* st, int t, uint32_
   st->amax[t] = A;
   st->scale[t] = scale_from_amax(A);
   st->inv_scale[t] = inv_scale_from_amax(A);
-  st->cur[t] = 0u;
   return A != rest;
+}
+
+// The pending observation of tensor t: the maximum over its stripes (fp32 bit images),
+// which are cleared.
+__device__ __forceinline__ float take_observation(fp8attn_state* st, int t) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int s = 0; s < FP8ATTN_CUR_STRIPES; ++s) {
+    const uint32_t v = st->cur[s][t];
+    m = v > m ? v : m;
+  }
+#pragma unroll
+  for (int s = 0; s < FP8ATTN_CUR_STRIPES; ++s) st->cur[s][t] = 0u;
+  return __uint_as_float(m);
+}
+
+// Folds a block's maximum (fp32 bit image of a non-negative value, which orders like the
+// value) into *word with one device atomic, skipped when the word already holds at least
+// as much. Atomics on one 64-byte line serialise (about 13 ns each), hence the stripes of
+// the state's cur and this filter; its read bypasses the XCD's L2 (system scope): an L2
+// copy of a word that other XCDs' atomics keep raising can stay stale for the whole launch.
+__device__ __forceinline__ void fold_max(uint32_t* word, uint32_t img) {
+  if (img != 0 && img > __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM))
+    atomicMax(word, img);
 }
 
 __device__ __forceinline__ float clamp_e4m3(float y) {

@@ -12,7 +12,8 @@
 #include "fp8attn.h"
 #include "launch.h"
 
-static_assert(sizeof(fp8attn_state) == 256, "fp8attn_state is part of the ABI");
+static_assert(sizeof(fp8attn_state) == 1280, "fp8attn_state is part of the ABI");
+static_assert(offsetof(fp8attn_state, cur) % 64 == 0, "each stripe is a 64-byte line");
 
 namespace {
 

@@ -16,8 +16,9 @@ static-scale kernel does with a margin; loading hands the numbers back unchanged
 mode with margin 1), so a saved-then-loaded layer quantises exactly as a layer built with
 static_amax = window maximum and margin = 1.5.
 
-Host I/O only: the numbers come from a layer's device state (one 256-byte copy) and go to
-AttentionLayer(static_amax=..., margin=1.0); nothing here runs per forward.
+Host I/O only: the numbers come from a layer's device state (one copy of the state
+bytes) and go to AttentionLayer(static_amax=..., margin=1.0); nothing here runs per
+forward.
 """
 import json
 import math

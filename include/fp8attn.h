@@ -79,9 +79,6 @@ typedef enum fp8attn_status {
  * by copying bytes. Tensor index t: 0 = Q, 1 = K, 2 = V.
  *   ring[t][s]   amax observed by dynamic forward number f is stored in slot f mod 16
  *                (vLLM docs "FP8 ViT Encoder Attention", "Usage": 16 observed values).
- *   cur[t]       fp32 bit image of the amax being gathered by fp8attn_observe_amax
- *                (a non-negative float compares like its bit pattern); cleared by
- *                fp8attn_scales.
  *   count        number of dynamic scale updates so far (the next slot is count mod 16).
  *   scale[t]     dequantisation scale A/448 of the current forward.
  *   inv_scale[t] quantisation multiplier 448/A of the current forward.
@@ -89,19 +86,28 @@ typedef enum fp8attn_status {
  *   moved        bit t set when the last dynamic scale update changed tensor t's window
  *                maximum, i.e. its new observation exceeded the other 15 slots (0 after a
  *                static update); fp8attn_quantize_dynamic re-quantises exactly those.
+ *   cur[s][t]    (t < 3) the amax being gathered by fp8attn_observe_amax, striped: the
+ *                observation of tensor t is the maximum over the FP8ATTN_CUR_STRIPES
+ *                stripes s of these fp32 bit images (a non-negative float compares like
+ *                its bit pattern). Each block of an observing kernel folds its maximum
+ *                into the stripe of its block index, and each stripe is a 64-byte line
+ *                of its own (words 3..15 are unused), because device atomics on one line
+ *                serialise. Gathered and cleared by fp8attn_scales.
  */
+#define FP8ATTN_CUR_STRIPES 16
+
 typedef struct fp8attn_state {
   float ring[3][FP8ATTN_RING_SLOTS];
-  uint32_t cur[3];
   uint32_t count;
   float scale[3];
   float inv_scale[3];
   float amax[3];
   uint32_t moved;
-  uint32_t reserved[2];
+  uint32_t reserved[5];
+  uint32_t cur[FP8ATTN_CUR_STRIPES][16];
 } fp8attn_state;
 
-/* Size in bytes of fp8attn_state (256). */
+/* Size in bytes of fp8attn_state (1280). */
 size_t fp8attn_state_bytes(void);
 
 /*
@@ -116,8 +122,8 @@ int fp8attn_state_reset(void* state, void* stream);
  * (vLLM docs "FP8 ViT Encoder Attention", "Usage": the amax of Q, K and V is observed on
  * every dynamic forward). One launch reads all three bf16 tensors of n elements each
  * (n = total_tokens * num_heads * head_dim; 16-byte aligned pointers) and folds
- * max|x| into state->cur[t] with one atomic per block and tensor. The result is exact
- * (a bf16 magnitude). n = 0 observes 0. Must be followed by exactly one fp8attn_scales.
+ * max|x| into the striped state->cur[.][t] with at most one atomic per block and tensor.
+ * The result is exact (a bf16 magnitude). n = 0 observes 0. Must be followed by exactly one fp8attn_scales.
  * Errors: EINVAL for a NULL state, NULL tensor with n > 0, n < 0, or a misaligned pointer.
  */
 int fp8attn_observe_amax(void* state, const void* q, const void* k, const void* v, int64_t n,
@@ -126,13 +132,14 @@ int fp8attn_observe_amax(void* state, const void* q, const void* k, const void* 
 /*
  * Compute this forward's scales (vLLM docs "FP8 ViT Encoder Attention", "Usage" and
  * "Scale file format").
- *   mode FP8ATTN_DYNAMIC: ring[t][count mod 16] = cur[t]; A_t = max over the 16 slots
- *     (empty slots hold 0); count += 1. static_amax_host and margin are ignored.
+ *   mode FP8ATTN_DYNAMIC: ring[t][count mod 16] = the observation (the maximum of
+ *     cur[.][t]); A_t = max over the 16 slots (empty slots hold 0); count += 1.
+ *     static_amax_host and margin are ignored.
  *   mode FP8ATTN_STATIC: A_t = fp32(static_amax_host[t] * margin); the ring and count are
  *     left unchanged. static_amax_host is a HOST array of 3 floats (q, k, v calibrated
  *     amax); margin > 0 (the pages' default is 1.5, FP8ATTN_DEFAULT_MARGIN).
  *   Both modes: A' = max(A_t, 2^-64); scale[t] = fp32(A'/448) and inv_scale[t] =
- *     fp32(448/A'), each a correctly rounded division; cur[t] is cleared.
+ *     fp32(448/A'), each a correctly rounded division; cur is cleared.
  * One single-wave launch; no host synchronisation.
  * Errors: EINVAL for a NULL state, an unknown mode, a NULL static_amax_host in static
  * mode, a static amax that is negative or not finite, a margin that is not > 0 and finite.

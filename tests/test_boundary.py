@@ -41,9 +41,10 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_sizes(lib):
-    assert lib.fp8attn_state_bytes() == 256
+    assert lib.fp8attn_state_bytes() == 1280
     from fp8_dynamic_scaled_amd.api import STATE_DTYPE
-    assert STATE_DTYPE.itemsize == 256
+    assert STATE_DTYPE.itemsize == 1280
+    assert STATE_DTYPE.fields["cur"][1] % 64 == 0     # each stripe a 64-byte line
     T, B, H, D = 43200, 3, 16, 128
     Tp = (T + 127) // 128 * 128 + 128 * B
     assert lib.fp8attn_workspace_bytes(T, B, H, D) == 2 * T * H * D + H * D * Tp

@@ -2,7 +2,7 @@
 separate observe + scales + quantise calls, bit for bit.
 
 Both layers see the same inputs, forward after forward; after every forward the workspace
-bytes (Q8, K8, V8t), the whole 256-byte state and the attention output must be equal. The
+bytes (Q8, K8, V8t), the whole state and the attention output must be equal. The
 sequence exercises: the first forward (empty ring, every tensor re-quantised), repeated
 inputs (window maximum unchanged, no re-quantisation), a rising maximum on one tensor only,
 falling draws that push the old maximum out of the 16-slot window, an all-zero tensor and

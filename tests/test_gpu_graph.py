@@ -6,7 +6,7 @@ scales, quantise, attend) is a kernel launch with no allocation, copy, memset or
 sync, so the forward can be captured once and replayed. The test captures one forward of
 a layer, then replays it on fresh inputs copied into the captured buffers, with eager
 work and synchronisations between replays, and checks every replay bit for bit (output
-and the whole 256-byte state, ring included) against an eager twin layer fed the same
+and the whole state, ring included) against an eager twin layer fed the same
 inputs.
 """
 import pytest

@@ -89,7 +89,7 @@ def test_amax_tail_and_empty_through_c_abi():
         s = fa.read_state(st)
         for t in range(3):
             want = oracle.amax_bf16(bits(x[t][:n]))
-            got = float(np.array([s["cur"][t]], dtype=np.uint32).view(np.float32)[0])
+            got = float(np.array([s["cur"][:, t].max()], dtype=np.uint32).view(np.float32)[0])
             assert got == want, (n, t)
         fa.scales(st, "static", [1.0, 1.0, 1.0], 1.0)
     # n = 0 observes nothing: the dynamic scale then sees an all-zero window
