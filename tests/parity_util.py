@@ -138,10 +138,12 @@ def hw_bound_rows(q8, k8, v8, cu, scales_qkv, sm_scale, tokens, kv_block=KV_BLOC
     q8/k8/v8: E4M3 codes [T, H, d] (q8 needs only the requested rows). For row r the score
     of key j may be off by e_j = c * 2 * 2^-11 * max_c |q_c k_jc| (two 64-channel
     instructions); the running maximum by E = the largest e over the keys that hold a
-    block maximum. Each quantised weight then lies between the E4M3 codes of
-    P~_j * 448 * exp(-+(e_j + 2E)), and the rescale factors within exp(+-2E); the PV and
-    row-sum products add 2^-11 of their largest product per 64-key instruction; output
-    rounding to bf16 adds 2^-9 |O|.
+    block maximum. As in the online rule, the weight of key j in block b is quantised
+    relative to the running maximum m_b after that block, P~_j = exp(s_j - m_b) * 448, and
+    enters the output scaled by exp(m_b - m_final). Each quantised weight then lies between
+    the E4M3 codes of P~_j * exp(-+(e_j + 2E)), and the rescale factors within exp(+-2E);
+    the PV and row-sum products add 2^-11 of their largest product per 64-key instruction;
+    output rounding to bf16 adds 2^-9 |O|.
     """
     sq, sk, sv = scales_qkv[0][0], scales_qkv[1][0], scales_qkv[2][0]
     c = sq * sk * sm_scale
@@ -164,11 +166,17 @@ def hw_bound_rows(q8, k8, v8, cu, scales_qkv, sm_scale, tokens, kv_block=KV_BLOC
                 j0, j1 = bb * kv_block, min(S, (bb + 1) * kv_block)
                 am = np.argmax(s[:, j0:j1], axis=1) + j0
                 E = np.maximum(E, e[np.arange(len(rows)), am][:, None])
-            m = s.max(axis=1, keepdims=True)
-            pt = np.exp(s - m) * oracle.E4M3_MAX
-            lo8 = oracle.e4m3_decode(oracle.e4m3_encode(pt * np.exp(-(e + 2 * E))))
-            hi8 = oracle.e4m3_decode(oracle.e4m3_encode(pt * np.exp(e + 2 * E)))
-            p = oracle.e4m3_decode(oracle.e4m3_encode(pt))
+            m_final = s.max(axis=1, keepdims=True)
+            pt = np.zeros_like(s)                               # P~ against the running max
+            w = np.zeros_like(s)                                # its factor exp(m_b - m_final)
+            for bb in range(nblk):
+                j0, j1 = bb * kv_block, min(S, (bb + 1) * kv_block)
+                m_b = s[:, :j1].max(axis=1, keepdims=True)
+                pt[:, j0:j1] = np.exp(s[:, j0:j1] - m_b) * oracle.E4M3_MAX
+                w[:, j0:j1] = np.exp(m_b - m_final)
+            lo8 = oracle.e4m3_decode(oracle.e4m3_encode(pt * np.exp(-(e + 2 * E)))) * w
+            hi8 = oracle.e4m3_decode(oracle.e4m3_encode(pt * np.exp(e + 2 * E))) * w
+            p = oracle.e4m3_decode(oracle.e4m3_encode(pt)) * w
             L = p.sum(axis=1, keepdims=True)
             O = (p @ v) / L
             dw = (hi8 - lo8) + p * (np.exp(2 * E) - 1.0)
