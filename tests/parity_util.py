@@ -110,26 +110,35 @@ def cosine(a: np.ndarray, b: np.ndarray) -> float:
 MFMA_REL_ERR = 2.0 ** -11          # per instruction, relative to its largest |product|
 
 
+_NONNEG_VALUES = oracle.e4m3_decode(np.arange(0x7F, dtype=np.uint8))   # codes 0x00..0x7E
+_NONNEG_MIDS = (_NONNEG_VALUES[:-1] + _NONNEG_VALUES[1:]) / 2
+
+
+def encode_nonneg(a):
+    """E4M3 codes of non-negative values (RNE, saturating), by binary search over the 126
+    midpoints between consecutive codes: a value on a midpoint takes the even code, which
+    is the even mantissa (the low code bit is the low mantissa bit, and across a binade
+    edge the larger value has mantissa 0). Equal to oracle.e4m3_encode on a >= 0
+    (tests/test_hw_bound.py); used where the bound encodes millions of weights."""
+    a = np.asarray(a, dtype=np.float64)
+    i = np.searchsorted(_NONNEG_MIDS, a, side="left")
+    on_mid = (i < len(_NONNEG_MIDS)) & (a == _NONNEG_MIDS[np.minimum(i, len(_NONNEG_MIDS) - 1)])
+    i = np.where(on_mid & (i % 2 == 1), i + 1, i)
+    return i.astype(np.uint8)
+
+
 def _max_products(q, k):
-    """Upper bound on max_c |q[r,c] k[j,c]| for every (row, key), exact on the channels
-    that can hold the maximum. Exact channels: those where |k| reaches a quarter of its
-    global maximum (K's outlier channels) and, per row, those with |q_c| >= max|q|/4; the
-    remaining channels are bounded by max_rest |q_c| * max_rest |k_jc|. Inputs are E4M3
-    values, so every product is exact in float64."""
-    qa = np.abs(q).astype(np.float64)
-    ka = np.abs(k).astype(np.float64)
-    kcol = ka.max(axis=0)
-    kbig = kcol >= kcol.max() / 4
-    krest = ka[:, ~kbig].max(axis=1) if (~kbig).any() else np.zeros(k.shape[0])
-    out = np.empty((q.shape[0], k.shape[0]), dtype=np.float64)
-    for r in range(q.shape[0]):
-        big = kbig | (qa[r] >= qa[r].max() / 4)
-        exact = (ka[:, big] * qa[r, big][None, :]).max(axis=1)
-        rest = ~big
-        if rest.any():
-            exact = np.maximum(exact, qa[r, rest].max() * krest)
-        out[r] = exact
-    return out
+    """max_c |q[r,c] k[j,c]| for every (row, key), exactly: the inputs are E4M3 values, so
+    each product is exact in float32 (at most 8 significant bits, below 2^18), and so is
+    their maximum. One pass per channel over a [rows, keys] buffer."""
+    qa = np.abs(np.asarray(q, dtype=np.float64)).astype(np.float32).T.copy()   # [d, rows]
+    ka = np.abs(np.asarray(k, dtype=np.float64)).astype(np.float32).T.copy()   # [d, keys]
+    out = np.zeros((qa.shape[1], ka.shape[1]), dtype=np.float32)
+    tmp = np.empty_like(out)
+    for c in range(qa.shape[0]):
+        np.multiply(qa[c][:, None], ka[c][None, :], out=tmp)
+        np.maximum(out, tmp, out=out)
+    return out.astype(np.float64)
 
 
 def hw_bound_rows(q8, k8, v8, cu, scales_qkv, sm_scale, tokens, kv_block=KV_BLOCK):
@@ -169,14 +178,15 @@ def hw_bound_rows(q8, k8, v8, cu, scales_qkv, sm_scale, tokens, kv_block=KV_BLOC
             m_final = s.max(axis=1, keepdims=True)
             pt = np.zeros_like(s)                               # P~ against the running max
             w = np.zeros_like(s)                                # its factor exp(m_b - m_final)
+            m_b = np.full((len(rows), 1), -np.inf)
             for bb in range(nblk):
                 j0, j1 = bb * kv_block, min(S, (bb + 1) * kv_block)
-                m_b = s[:, :j1].max(axis=1, keepdims=True)
+                m_b = np.maximum(m_b, s[:, j0:j1].max(axis=1, keepdims=True))
                 pt[:, j0:j1] = np.exp(s[:, j0:j1] - m_b) * oracle.E4M3_MAX
                 w[:, j0:j1] = np.exp(m_b - m_final)
-            lo8 = oracle.e4m3_decode(oracle.e4m3_encode(pt * np.exp(-(e + 2 * E)))) * w
-            hi8 = oracle.e4m3_decode(oracle.e4m3_encode(pt * np.exp(e + 2 * E))) * w
-            p = oracle.e4m3_decode(oracle.e4m3_encode(pt)) * w
+            lo8 = oracle.e4m3_decode(encode_nonneg(pt * np.exp(-(e + 2 * E)))) * w
+            hi8 = oracle.e4m3_decode(encode_nonneg(pt * np.exp(e + 2 * E))) * w
+            p = oracle.e4m3_decode(encode_nonneg(pt)) * w
             L = p.sum(axis=1, keepdims=True)
             O = (p @ v) / L
             dw = (hi8 - lo8) + p * (np.exp(2 * E) - 1.0)

@@ -14,7 +14,7 @@ import math
 import numpy as np
 
 import oracle
-from parity_util import KV_BLOCK, MFMA_REL_ERR, _max_products, hw_bound_rows
+from parity_util import KV_BLOCK, MFMA_REL_ERR, _max_products, encode_nonneg, hw_bound_rows
 
 SM = float(np.float32(1.0 / math.sqrt(128)))
 
@@ -111,3 +111,26 @@ def test_bound_is_small_without_matrix_core_error(monkeypatch):
     O = _online((oracle.e4m3_decode(k) @ oracle.e4m3_decode(q)) * SM, oracle.e4m3_decode(v))
     # only the bf16 output rounding remains (plus the rescale term, zero with E = 0)
     assert np.all(b <= 2.0 ** -9 * np.abs(O) * (1 + 1e-9) + 1e-300)
+
+
+def test_fast_nonnegative_encoder_equals_the_oracle():
+    rng = np.random.default_rng(4)
+    vals = oracle.e4m3_decode(np.arange(0x7F, dtype=np.uint8))
+    mids = (vals[:-1] + vals[1:]) / 2
+    x = np.concatenate([
+        vals, mids,                                          # every code and every tie
+        np.nextafter(mids, 0), np.nextafter(mids, np.inf),   # just around each tie
+        [0.0, 448.0, 464.0, 465.0, 1e9, np.inf, 2.0 ** -10, 2.0 ** -11],
+        np.exp(rng.uniform(-25, 7, 200000)),                 # weights exp(s - m) * 448
+        rng.uniform(0, 500, 100000)])
+    assert np.array_equal(encode_nonneg(x), oracle.e4m3_encode(x))
+
+
+def test_max_products_brute_force():
+    rng = np.random.default_rng(5)
+    for _ in range(4):
+        out = 1 + 30 * (rng.random(128) < 0.03)
+        q = oracle.e4m3_decode(oracle.e4m3_encode(rng.standard_normal((9, 128)) * out))
+        k = oracle.e4m3_decode(oracle.e4m3_encode(rng.standard_normal((333, 128)) * 2))
+        want = np.abs(q[:, None, :] * k[None, :, :]).max(axis=2)
+        assert np.array_equal(_max_products(q, k), want)
