@@ -245,6 +245,9 @@ def regime(fa, dev, reps=7):
                              outliers=True))
              for name, ph, pw, n in RESOLUTIONS]
     cases.append(("DiT forward 57600 tokens, H=40", WORKLOADS["dit"]))
+    # one GPU's share of that forward under head (Ulysses) sharding of degree 4
+    cases.append(("DiT forward, one of 4 head shards (H=10)",
+                  Workload("dit-shard", 5, (0, 57600), 10, outliers=True)))
     for name, w in cases:
         q, k, v = make_qkv(w, 0, dev)
         cu = list(w.cu_seqlens)
