@@ -1,0 +1,73 @@
+"""GPU parity past 2^31 elements per tensor: 20 sequences of 56 000 tokens x 16 heads x 128
+channels (2.29 G elements, 4.6 GB of bf16 per tensor), within the per-sequence 32-bit
+limits of the C-ABI. Element offsets into Q, K, V, Q8, K8, V8t and the output then exceed
+2^31, and every kernel must address them with 64-bit arithmetic.
+
+Checked against the oracle: the amax (streamed through the host) and the ring/scales;
+the E4M3 bytes of the last 1 000 tokens of Q8 and K8 and of the last sequence's V8t
+columns for two heads; attention rows of the last sequence (sequences are independent, so
+the oracle sees only that sequence). The one-pass dynamic path produces the state and the
+workspace bytes checked here.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import fp8_dynamic_scaled_amd as fa
+from workloads import draw_tensor
+
+from parity_util import (MAX_ABS_TOL, MEAN_ABS_TOL, amax_exact, bf16_to_f64, bits, compare,
+                         oracle_fp8_rows, quant_lut)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+SM = fa.default_softmax_scale()
+S, B, H = 56000, 20, 16
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+@pytest.mark.timeout(600)
+def test_tensors_past_2_pow_31_elements():
+    T = S * B
+    assert T * H * 128 > 2 ** 31
+    say(f"large: {B} x {S} tokens, H={H}: {T * H * 128 / 1e9:.2f} G elements per tensor")
+    q, k, v = (draw_tensor(T, H, 128, 9100 + t, DEV) for t in range(3))
+    cu = [i * S for i in range(B + 1)]
+    cu_d = torch.tensor(cu, dtype=torch.int32, device=DEV)
+    layer = fa.AttentionLayer(DEV)
+    out = layer(q, k, v, cu_d, cu)
+    torch.cuda.synchronize()
+    say("  forward done; oracle amax (streamed)")
+
+    A = oracle.AmaxRing().update([amax_exact(t) for t in (q, k, v)])
+    s = fa.read_state(layer.state)
+    sc = [oracle.scale_pair(a) for a in A]
+    for t in range(3):
+        assert float(s["amax"][t]) == A[t]
+        assert float(s["scale"][t]) == sc[t][0] and float(s["inv_scale"][t]) == sc[t][1]
+
+    # bytes at the far end of the workspace
+    q8, k8, v8t = fa.split_workspace(layer._ws, T, B, H)
+    luts = [quant_lut(x[1]) for x in sc]
+    tail = slice(T - 1000, T)
+    assert np.array_equal(q8[tail].to("cpu").numpy(), luts[0][bits(q[tail])])
+    assert np.array_equal(k8[tail].to("cpu").numpy(), luts[1][bits(k[tail])])
+    lo, hi = cu[-2], cu[-1]
+    ps = fa.pad_start(lo, B - 1)
+    for h in (0, H - 1):
+        got = v8t[h, :, ps:ps + S].to("cpu").numpy()
+        assert np.array_equal(got, luts[2][bits(v[lo:hi, h])].T), h
+    say("  state and far-end bytes bit-exact")
+
+    # attention rows of the last sequence
+    rows = np.concatenate([np.arange(0, 48), np.arange(S - 48, S),
+                           np.random.default_rng(7).integers(0, S, 32)])
+    want = oracle_fp8_rows(q[lo:hi], k[lo:hi], v[lo:hi], [0, S], sc, SM, tokens=rows)
+    got = bf16_to_f64(out[torch.as_tensor(lo + rows, device=DEV)])
+    mx, mn = compare(got, want)
+    say(f"  last sequence, {len(rows)} rows: max-abs {mx:.3e} mean-abs {mn:.3e}")
+    assert mx <= MAX_ABS_TOL and mn <= MEAN_ABS_TOL
