@@ -324,6 +324,37 @@ def test_fp8_closed_forms():
     assert np.max(np.abs(got - want[None])) <= 2.0 ** -8 * np.max(np.abs(want)) + 1e-6
 
 
+def test_one_key_takes_all_the_weight():
+    say("closed form: one key dominates -> every other weight is 0, the output is its V row")
+    lens, H = [200, 97], 2
+    T = sum(lens)
+    cu = [0, lens[0], T]
+    g = torch.Generator(device=DEV).manual_seed(21)
+    q = torch.full((T, H, 128), 2.0, device=DEV).to(torch.bfloat16)
+    k = (torch.randn((T, H, 128), device=DEV, generator=g) * 0.1).to(torch.bfloat16)
+    v = torch.randn((T, H, 128), device=DEV, generator=g).to(torch.bfloat16)
+    # the dominant key: the last of sequence 0 (its ragged last tile), the first of
+    # sequence 1; score gap about 180 >> ln(448 * 2^10), so every other E4M3 weight is 0
+    dom = [cu[1] - 1, cu[1]]
+    for j in dom:
+        k[j] = 8.0
+    out, layer = _run_fp8(q, k, v, cu)
+    s = fa.read_state(layer.state)
+    v8 = quant_lut(float(s["inv_scale"][2]))[bits(v)]
+    got = bf16_to_f64(out)
+    for i, j in enumerate(dom):
+        want = oracle.e4m3_decode(v8[j]) * float(s["scale"][2])      # [H, D]
+        # the kernel forms 448 * v8_j * fp32(scale_v / 448) and rounds it to bf16 once: at
+        # most one bf16 step from the exact row
+        err = np.abs(got[cu[i]:cu[i + 1]] - want[None])
+        assert np.all(err <= 2.0 ** -8 * np.abs(want)[None] + 1e-30), i
+    skip = fa.forward(None, q, k, v, _cu_dev(cu), cu, skip=True)
+    got_b = bf16_to_f64(skip)
+    vb = bf16_to_f64(v)
+    for i, j in enumerate(dom):
+        assert np.array_equal(got_b[cu[i]:cu[i + 1]], np.broadcast_to(vb[j], (lens[i], H, 128))), i
+
+
 def test_packed_equals_separate_calls():
     say("block-diagonal isolation: packed vs per-sequence calls (static scales)")
     lens, H = [130, 0, 257, 64, 1], 2
