@@ -392,7 +392,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp8_e4m3 (fp32 accumulate)",
-        "data": "synthetic (seeded bf16 N(0,1), 0.1% of hidden columns x20)",
+        "data": f"synthetic (seeded bf16; {w.description.split(';')[0].split(', ', 2)[-1]})",
         "config": {"workload": f"{w.name}: {w.description}", "num_seqs": B, "seq_len": w.seq_lens[0],
                    "num_heads": H, "head_dim": D, "causal": False, "scaling": "dynamic 16-slot ring"},
         "roofline": {"bound": "mfma", "kernel": "attn_fp8_kernel",
