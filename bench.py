@@ -11,8 +11,10 @@ are timed afterwards for reference, then the BF16 skip-path kernel on the same b
 heads, head_dim 128, bf16 N(0,1) with x20 outlier columns).
 
 Prints ONE JSON line. value = attention FLOPs of the step (4 * S^2 * d * H) / step time,
-in TFLOP/s. Per-kernel durations come from HIP events recorded on the stream the kernels
-run on (torch's current stream), around each launch of the timed steps (mean and median).
+in TFLOP/s. Kernel durations come from HIP events recorded on the stream the kernels run
+on (torch's current stream): around each launch of the timed steps (mean and median), and,
+for the two attention kernels, around back-to-back bursts of launches (the roofline figure
+and the FP8/BF16 ratio use those).
 
 The quantisation rate is also measured where the inputs cannot sit in the 256 MB
 Infinity Cache: on the same batch with a 512 MB device write before every launch (the
@@ -353,6 +355,19 @@ def main():
     per = {k2: sum(v2) / len(v2) for k2, v2 in samples.items()}            # ms per launch (mean)
     per_median = {k2: sorted(v2)[len(v2) // 2] for k2, v2 in samples.items()}
 
+    # both attention kernels as back-to-back bursts between one event pair, so that the
+    # per-launch event packets and dispatch fences of the step loop do not enter the
+    # kernel time (the roofline and the FP8/BF16 ratio use these)
+    fa.quantize_dynamic(st, q, k, v, cu_d, cu, workspace=ws)
+    b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    b0.record()
+    for _ in range(args.steps):
+        fa.attend(st, ws, cu_d, cu, H, out=out)
+    b1.record()
+    torch.cuda.synchronize()
+    ms_fp8_burst = b0.elapsed_time(b1) / args.steps
+
     # BF16 skip-path kernel on the same batch
     for _ in range(args.warmup):
         fa.forward(None, q, k, v, cu_d, cu, skip=True, out=out)
@@ -367,7 +382,7 @@ def main():
 
     cold = None if args.no_cold_quant else cold_quant(fa, w, q, k, v, cu_d, cu, st, ws, dev)
 
-    attn_tflops = flops / (per["attn_fp8"] * 1e-3) / 1e12
+    attn_tflops = flops / (ms_fp8_burst * 1e-3) / 1e12
     quant_gbs = (3 * n * 3) / (per["quantize"] * 1e-3) / 1e9
     dyn_gbs = (3 * n * 3) / (per["quantize_dynamic"] * 1e-3) / 1e9
     amax_gbs = (3 * n * 2) / (per["amax"] * 1e-3) / 1e9
@@ -407,7 +422,12 @@ def main():
         "attn_bf16_ms": round(ms_bf16, 5),
         "attn_bf16_tflops": round(bf16_tflops, 2),
         "attn_bf16_frac_bf16_peak": round(bf16_tflops / BF16_PEAK_TFLOPS, 4),
-        "fp8_over_bf16_speedup": round(ms_bf16 / per["attn_fp8"], 3),
+        "attn_fp8_ms": round(ms_fp8_burst, 5),
+        "fp8_over_bf16_speedup": round(ms_bf16 / ms_fp8_burst, 3),
+        "kernel_times_note": "attn_fp8_ms and attn_bf16_ms: back-to-back launches between one "
+                             "HIP event pair (the roofline uses attn_fp8_ms); kernels_ms: HIP "
+                             "events around each launch of the timed steps, which add the "
+                             "event packets and dispatch fences of each launch",
         "quant_gbs": round(quant_gbs, 1),
         "dynamic_quant_gbs": round(dyn_gbs, 1),
         "dynamic_quant_note": "fp8attn_quantize_dynamic (quantise + observe, scales, "
