@@ -11,10 +11,15 @@ are timed afterwards for reference, then the BF16 skip-path kernel on the same b
 heads, head_dim 128, bf16 N(0,1) with x20 outlier columns).
 
 Prints ONE JSON line. value = attention FLOPs of the step (4 * S^2 * d * H) / step time,
-in TFLOP/s. Kernel durations come from HIP events recorded on the stream the kernels run
-on (torch's current stream): around each launch of the timed steps (mean and median), and,
-for the two attention kernels, around back-to-back bursts of launches (the roofline figure
-and the FP8/BF16 ratio use those).
+in TFLOP/s, the step time being the wall time of K back-to-back steps between two device
+synchronisations. Before them, an untimed warm-up of at least W steps and at least
+--settle-ms of continuous work: after an idle stretch the GPU's clock ramps up over the
+first tens of milliseconds of work (at the kernel point a step averages about 450 us over
+its first 20 runs and settles near 325 us after about 50 ms), and the benchmark reports the
+sustained rate. Kernel durations come from HIP events recorded on the stream the kernels
+run on (torch's current stream), in loops of their own after the timed steps: around each
+launch of K more steps (mean and median), and, for the two attention kernels, around
+back-to-back bursts of K launches (the roofline figure and the FP8/BF16 ratio use those).
 
 The quantisation rate is also measured where the inputs cannot sit in the 256 MB
 Infinity Cache: on the same batch with a 512 MB device write before every launch (the
@@ -45,8 +50,11 @@ ATTN_SRC = os.path.join(ROOT, "fp8_dynamic_scaled_amd", "csrc", "attn_fp8.hip")
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--settle-ms", type=float, default=200.0,
+                    help="the untimed warm-up also lasts at least this long (ms of "
+                         "continuous work), past the GPU clock's ramp after idle")
     ap.add_argument("--workload", default="kernel")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing on the host cores")
@@ -224,19 +232,50 @@ RESOLUTIONS = (("448x448", 28, 28, 3), ("HD 720x1280", 45, 80, 3),
                ("448x448 x64", 28, 28, 64), ("256x256 x256", 16, 16, 256))
 
 
-def _median_ms(fn, reps):
+def settle(fns, min_rounds, ms):
+    """Untimed warm-up: rounds of `fns` until at least `min_rounds` rounds have run and at
+    least `ms` milliseconds of wall time have passed with the GPU kept busy (the host waits
+    for the device every ~5 ms of work, so it never runs far ahead of it)."""
     import torch
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
-    for e in ev:
-        e[0].record()
-        fn()
-        e[1].record()
     torch.cuda.synchronize()
-    t = sorted(e[0].elapsed_time(e[1]) for e in ev)
+    t0 = time.perf_counter()
+    for f in fns:
+        f()
+    torch.cuda.synchronize()
+    est = max(time.perf_counter() - t0, 1e-6)
+    chunk = max(1, int(5e-3 / est))
+    rounds = 1
+    while rounds < min_rounds or (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(chunk):
+            for f in fns:
+                f()
+        rounds += chunk
+        torch.cuda.synchronize()
+    return rounds
+
+
+def _burst_ms(fn, n):
+    """ms per call of `fn` over n back-to-back calls between one HIP event pair."""
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
+def _median_burst_ms(fn, burst_ms=25.0, bursts=3):
+    """Median over `bursts` bursts of back-to-back calls, each about `burst_ms` long (at
+    least 5 calls)."""
+    est = _burst_ms(fn, 2)
+    n = max(5, min(2000, math.ceil(burst_ms / max(est, 1e-3))))
+    t = sorted(_burst_ms(fn, n) for _ in range(bursts))
     return t[len(t) // 2]
 
 
-def regime(fa, dev, reps=7):
+def regime(fa, dev, settle_ms=60.0):
     """FP8 dynamic step (one-pass quantise + FP8 attention) against the BF16 kernel on
     3-image batches per resolution (16 heads, bf16 N(0,1) with x20 outlier columns), and on
     one forward of the DiT video workload (57600 tokens, 40 heads)."""
@@ -273,10 +312,8 @@ def regime(fa, dev, reps=7):
         def bf16():
             fa.forward(None, q, k, v, cu_d, cu, skip=True, out=out)
 
-        for _ in range(3):
-            fp8_step()
-            bf16()
-        t_step, t_q, t_a, t_b = (_median_ms(f, reps) for f in (fp8_step, quant, attn, bf16))
+        settle([fp8_step, bf16], 3, settle_ms)
+        t_step, t_q, t_a, t_b = (_median_burst_ms(f) for f in (fp8_step, quant, attn, bf16))
         rows[name] = {"tokens_per_image": w.seq_lens[0], "images": w.num_seqs, "heads": H,
                       "fp8_step_ms": round(t_step, 4), "quantize_dynamic_ms": round(t_q, 4),
                       "attn_fp8_ms": round(t_a, 4), "attn_bf16_ms": round(t_b, 4),
@@ -331,16 +368,20 @@ def main():
         fa.quantize(st, q, k, v, cu_d, cu, workspace=ws)
         ev[3].record()
 
-    for _ in range(args.warmup):
-        step()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    warm_rounds = settle([step], args.warmup, args.settle_ms)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
+    for _ in range(args.steps):
+        step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
+
+    # per-kernel durations: K more steps with events around each launch (not timed above)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
     names = ("quantize_dynamic", "attn_fp8")
     samples = {k2: [e[i].elapsed_time(e[i + 1]) for e in evs] for i, k2 in enumerate(names)}
 
@@ -368,9 +409,9 @@ def main():
     torch.cuda.synchronize()
     ms_fp8_burst = b0.elapsed_time(b1) / args.steps
 
-    # BF16 skip-path kernel on the same batch
-    for _ in range(args.warmup):
-        fa.forward(None, q, k, v, cu_d, cu, skip=True, out=out)
+    # BF16 skip-path kernel on the same batch, after a warm-up of its own
+    settle([lambda: fa.forward(None, q, k, v, cu_d, cu, skip=True, out=out)], args.warmup,
+           args.settle_ms)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record()
@@ -402,6 +443,8 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_steps_run": warm_rounds,
+        "settle_ms": args.settle_ms,
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -424,10 +467,11 @@ def main():
         "attn_bf16_frac_bf16_peak": round(bf16_tflops / BF16_PEAK_TFLOPS, 4),
         "attn_fp8_ms": round(ms_fp8_burst, 5),
         "fp8_over_bf16_speedup": round(ms_bf16 / ms_fp8_burst, 3),
-        "kernel_times_note": "attn_fp8_ms and attn_bf16_ms: back-to-back launches between one "
-                             "HIP event pair (the roofline uses attn_fp8_ms); kernels_ms: HIP "
-                             "events around each launch of the timed steps, which add the "
-                             "event packets and dispatch fences of each launch",
+        "kernel_times_note": "attn_fp8_ms and attn_bf16_ms: K back-to-back launches between "
+                             "one HIP event pair (the roofline uses attn_fp8_ms); kernels_ms: "
+                             "HIP events around each launch of K further steps, which add the "
+                             "event packets and dispatch fences of each launch; all after the "
+                             "warm-up",
         "quant_gbs": round(quant_gbs, 1),
         "dynamic_quant_gbs": round(dyn_gbs, 1),
         "dynamic_quant_note": "fp8attn_quantize_dynamic (quantise + observe, scales, "
@@ -443,7 +487,8 @@ def main():
     if not args.no_regime:
         result["resolution_sweep"] = regime(fa, dev)
         result["resolution_sweep_note"] = (
-            "median of 7; fp8_step = fp8attn_quantize_dynamic + fp8attn_attend (dynamic "
+            "per case: 60 ms of alternating FP8 steps and BF16 calls as warm-up, then for "
+            "each figure the median of 3 bursts of back-to-back calls of about 25 ms; fp8_step = fp8attn_quantize_dynamic + fp8attn_attend (dynamic "
             "scaling, window maximum steady), attn_bf16 = the skip-path kernel; 3 images "
             "per request unless the name says x N, 16-pixel patches, H=16 (DiT: one "
             "forward, H=40)")
