@@ -94,6 +94,16 @@ __device__ __forceinline__ void fold_max(uint32_t* word, uint32_t img) {
     atomicMax(word, img);
 }
 
+// The same fold with no filter read: an atomic whose result is unused is posted, so the
+// wave does not wait for it, whereas the filter's L2-bypassing read makes it wait a
+// memory round trip. Where blocks are short and their tails count (the quantise pass that
+// observes the amax while it quantises), this is the cheaper form: 31 instead of 36 us for
+// the one-pass dynamic quantisation of 8192 tokens x 16 heads. The amax kernel keeps the
+// filter (1 % faster there).
+__device__ __forceinline__ void post_max(uint32_t* word, uint32_t img) {
+  if (img != 0) atomicMax(word, img);
+}
+
 __device__ __forceinline__ float clamp_e4m3(float y) {
   return __builtin_fminf(__builtin_fmaxf(y, -kE4M3Max), kE4M3Max);
 }

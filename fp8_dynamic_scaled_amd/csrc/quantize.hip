@@ -69,7 +69,7 @@ __device__ __forceinline__ uint32_t absmax8(uint32_t m, const uint4& r) {
 }
 
 // Block-wide max of per-thread 16-bit magnitudes; thread 0 folds the result into the
-// block's stripe of the pending observation state->cur (fp32 bit image, fold_max).
+// block's stripe of the pending observation state->cur (fp32 bit image, post_max).
 __device__ __forceinline__ void publish_max(fp8attn_state* st, int t, uint32_t m, uint32_t* red) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
@@ -84,7 +84,7 @@ __device__ __forceinline__ void publish_max(fp8attn_state* st, int t, uint32_t m
     uint32_t b = red[0];
 #pragma unroll
     for (int w = 1; w < kThreads / 64; ++w) b = red[w] > b ? red[w] : b;
-    fold_max(&st->cur[blockIdx.x % FP8ATTN_CUR_STRIPES][t], b << 16);
+    post_max(&st->cur[blockIdx.x % FP8ATTN_CUR_STRIPES][t], b << 16);
   }
 }
 
