@@ -220,9 +220,9 @@ def test_quantize_every_bf16_pattern(amax):
 
 
 # --------------------------------------------------------------------------- attention
-def _run_fp8(q, k, v, cu, static=None, margin=1.5):
+def _run_fp8(q, k, v, cu, static=None, margin=1.5, softmax_scale=0.0):
     layer = fa.AttentionLayer(DEV, static_amax=static, margin=margin)
-    out = layer(q, k, v, _cu_dev(cu), cu)
+    out = layer(q, k, v, _cu_dev(cu), cu, softmax_scale=softmax_scale)
     torch.cuda.synchronize()
     return out, layer
 
@@ -297,6 +297,43 @@ def test_bf16_attention_all_rows(lens, H):
     _assert_close("bf16 vs oracle", got, want)
     say(f"  cosine {cosine(got, want):.6f}")
     assert cosine(got, want) >= 0.9999
+
+
+@pytest.mark.parametrize("sm", [0.02, 0.3])
+def test_explicit_softmax_scale(sm):
+    # the softmax scale is an argument of the boundary: a flatter (0.02) and a much sharper
+    # (0.3, 3.4 x 1/sqrt(128)) softmax, both paths, all rows; the kernels use it as binary32
+    lens, H = [300, 64, 129], 2
+    say(f"explicit softmax scale {sm}: lens={lens} H={H}")
+    q, k, v, cu = random_varlen(lens, H, seed=91, device=DEV)
+    sm32 = float(np.float32(sm))
+    out, _ = _run_fp8(q, k, v, cu, softmax_scale=sm)
+    sc = [oracle.scale_pair(a) for a in _amax3(q, k, v)]
+    got, want = bf16_to_f64(out), oracle_fp8_rows(q, k, v, cu, sc, sm32)
+    # the score error of the FP8 matrix core grows with the scale, so elements are held to
+    # the stated tolerance or to the per-element hardware bound
+    luts = [quant_lut(x[1]) for x in sc]
+    toks = np.arange(q.shape[0])
+    bound = hw_bound_rows(luts[0][bits(q)], luts[1][bits(k)], luts[2][bits(v)], cu, sc, sm32,
+                          toks)
+    st = check_rows(got, want, bound, v_channel_std(v)[None])
+    say(f"  fp8 vs oracle: {st}")
+    assert st["ok"], st
+    bout = fa.forward(None, q, k, v, _cu_dev(cu), cu, softmax_scale=sm, skip=True)
+    torch.cuda.synchronize()
+    _assert_close("bf16 vs oracle", bf16_to_f64(bout), oracle_ref_rows(q, k, v, cu, sm32))
+
+
+def test_nonpositive_softmax_scale_selects_the_default():
+    # softmax_scale <= 0 means 1/sqrt(head_dim): bit-identical to passing that value
+    q, k, v, cu = random_varlen([200, 77], 2, seed=92, device=DEV)
+    say("softmax scale <= 0 -> 1/sqrt(128)")
+    outs = [_run_fp8(q, k, v, cu, softmax_scale=s)[0] for s in (0.0, -1.0, SM)]
+    bouts = [fa.forward(None, q, k, v, _cu_dev(cu), cu, softmax_scale=s, skip=True)
+             for s in (0.0, -1.0, SM)]
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[2]) and torch.equal(outs[1], outs[2])
+    assert torch.equal(bouts[0], bouts[2]) and torch.equal(bouts[1], bouts[2])
 
 
 def test_fp8_closed_forms():
