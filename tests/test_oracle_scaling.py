@@ -67,9 +67,13 @@ def test_scale_file_worked_example():
     # static mode: A = fp32(calibrated amax * margin); margin default 1.5
     assert g["margin_default"] == 1.5
     assert oracle.static_amax([2.0, 4.0, 1.0], g["margin_default"]) == [3.0, 6.0, 1.5]
-    # a calibrated amax of 224/1.5 reproduces the file's q entry up to binary32 rounding
+    # a calibrated amax of 224/1.5 reproduces the file's q entry: binary32(224/1.5) times 1.5
+    # is exactly 224 - 2^-17, half a binary32 step below 224, a tie that binary32 rounding
+    # settles on 224 (even significand); without that rounding A would stay 224 - 2^-17
+    c = float(np.float32(224.0 / 1.5))
+    assert c * 1.5 == 224.0 - 2.0 ** -17
     A = oracle.static_amax([224.0 / 1.5, 1.0, 1.0])[0]
-    assert abs(A - 224.0) <= 224.0 * 2.0 ** -23
+    assert A == 224.0
 
 
 def test_zero_amax_floor():
@@ -150,3 +154,4 @@ def test_quantize_vs_torch_library(seed):
         y = x.float() * torch.tensor(inv, dtype=torch.float32)
         want = y.clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
         assert np.array_equal(oracle.quantize_bf16(bits, inv), want)
+
