@@ -324,6 +324,38 @@ def test_explicit_softmax_scale(sm):
     _assert_close("bf16 vs oracle", bf16_to_f64(bout), oracle_ref_rows(q, k, v, cu, sm32))
 
 
+def test_two_layers_on_two_streams_concurrently():
+    # the library keeps no global state: two layers, each with its own state and workspace,
+    # running three dynamic forwards at once on two streams give the outputs and states
+    # they give one after the other on one stream
+    qa, ka, va, cua = random_varlen([700, 333], 4, seed=93, device=DEV)
+    qb, kb, vb, cub = random_varlen([512, 1, 900], 4, seed=94, device=DEV)
+    cua_d, cub_d = _cu_dev(cua), _cu_dev(cub)
+    torch.cuda.synchronize()
+    say("two layers, two streams, three dynamic forwards each")
+
+    def run(stream_a, stream_b):
+        la, lb = fa.AttentionLayer(DEV), fa.AttentionLayer(DEV)
+        torch.cuda.synchronize()                          # states zeroed on this stream
+        outs = []
+        for _ in range(3):
+            with torch.cuda.stream(stream_a):
+                oa = la(qa, ka, va, cua_d, cua)
+            with torch.cuda.stream(stream_b):
+                ob = lb(qb, kb, vb, cub_d, cub)
+            outs.append((oa, ob))
+        torch.cuda.synchronize()
+        return outs, la.state.clone(), lb.state.clone()
+
+    main = torch.cuda.current_stream()
+    seq_outs, seq_sa, seq_sb = run(main, main)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()     # default priority
+    con_outs, con_sa, con_sb = run(s1, s2)
+    for (a0, b0), (a1, b1) in zip(seq_outs, con_outs):
+        assert torch.equal(a0, a1) and torch.equal(b0, b1)
+    assert torch.equal(seq_sa, con_sa) and torch.equal(seq_sb, con_sb)
+
+
 def test_nonpositive_softmax_scale_selects_the_default():
     # softmax_scale <= 0 means 1/sqrt(head_dim): bit-identical to passing that value
     q, k, v, cu = random_varlen([200, 77], 2, seed=92, device=DEV)
