@@ -44,6 +44,14 @@ def _need_cuda(name, t, dtype=None):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _need_state(state):
+    """A state must be a contiguous uint8 device tensor of at least fp8attn_state_bytes():
+    the library only sees its address, so a shorter tensor would be written past its end."""
+    _need_cuda("state", state, torch.uint8)
+    if state.numel() < STATE_DTYPE.itemsize:
+        raise ValueError(f"state must hold {STATE_DTYPE.itemsize} bytes, got {state.numel()}")
+
+
 def _cu_host(cu_seqlens: torch.Tensor, cu_seqlens_host) -> np.ndarray:
     if cu_seqlens_host is None:
         # convenience path: one device -> host copy; pass the host copy to avoid it
@@ -65,7 +73,7 @@ def workspace_bytes(total_tokens: int, num_seqs: int, num_heads: int,
 
 
 def state_reset(state: torch.Tensor) -> None:
-    _need_cuda("state", state, torch.uint8)
+    _need_state(state)
     check("fp8attn_state_reset", _lib.load().fp8attn_state_reset(_ptr(state), _stream(state.device)))
 
 
@@ -85,7 +93,7 @@ def read_state(state: torch.Tensor) -> dict:
 
 
 def observe_amax(state: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor) -> None:
-    _need_cuda("state", state, torch.uint8)
+    _need_state(state)
     for name, t in (("q", q), ("k", k), ("v", v)):
         _need_cuda(name, t, torch.bfloat16)
     if not (q.numel() == k.numel() == v.numel()):
@@ -97,7 +105,7 @@ def observe_amax(state: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch
 
 def scales(state: torch.Tensor, mode: str = "dynamic", static_amax: Optional[Sequence[float]] = None,
            margin: float = DEFAULT_MARGIN) -> None:
-    _need_cuda("state", state, torch.uint8)
+    _need_state(state)
     if mode == "dynamic":
         m, arr = FP8ATTN_DYNAMIC, None
     elif mode == "static":
@@ -133,6 +141,7 @@ def quantize(state, q, k, v, cu_seqlens, cu_seqlens_host=None,
              workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Quantise into the FP8 workspace layout (Q8 | K8 | V8t); returns the workspace."""
     host, T, H, D = _varlen_args(q, k, v, cu_seqlens, cu_seqlens_host)
+    _need_state(state)
     B = host.shape[0] - 1
     need = workspace_bytes(T, B, H, D)
     if workspace is None:
@@ -155,7 +164,7 @@ def quantize_dynamic(state, q, k, v, cu_seqlens, cu_seqlens_host=None,
     need = workspace_bytes(T, B, H, D)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    _need_cuda("state", state, torch.uint8)
+    _need_state(state)
     _need_cuda("workspace", workspace, torch.uint8)
     check("fp8attn_quantize_dynamic",
           _lib.load().fp8attn_quantize_dynamic(_ptr(state), _ptr(q), _ptr(k), _ptr(v),
@@ -185,7 +194,7 @@ def attend(state, workspace, cu_seqlens, cu_seqlens_host, num_heads: int,
            softmax_scale: float = 0.0, out: Optional[torch.Tensor] = None,
            head_dim: int = HEAD_DIM) -> torch.Tensor:
     """FP8 attention on a workspace filled by quantize() (no quantisation step)."""
-    _need_cuda("state", state, torch.uint8)
+    _need_state(state)
     _need_cuda("workspace", workspace, torch.uint8)
     _need_cuda("cu_seqlens", cu_seqlens, torch.int32)
     host = _cu_host(cu_seqlens, cu_seqlens_host)
@@ -222,7 +231,7 @@ def forward(state, q, k, v, cu_seqlens, cu_seqlens_host=None, softmax_scale: flo
     if not skip:
         if state is None:
             raise ValueError("the FP8 path needs a state")
-        _need_cuda("state", state, torch.uint8)
+        _need_state(state)
         need = workspace_bytes(T, B, H, D)
         if workspace is None:
             workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)

@@ -191,3 +191,19 @@ def test_kv_block_constant_agrees():
     from parity_util import KV_BLOCK as ORACLE_BLOCK
     m = re.search(r"#define FP8ATTN_KV_BLOCK (\d+)", open(HEADER).read())
     assert int(m.group(1)) == fa.KV_BLOCK == ORACLE_BLOCK == 64
+
+
+def test_binding_rejects_host_tensors_before_any_gpu_call():
+    # the Python binding refuses host memory (and non-tensors) for every device argument,
+    # before the library sees an address
+    import torch
+    q = torch.zeros(8, 2, 128, dtype=torch.bfloat16)
+    cu = torch.tensor([0, 8], dtype=torch.int32)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        fa.forward(None, q, q, q, cu, [0, 8], skip=True)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        fa.quantize(torch.zeros(1280, dtype=torch.uint8), q, q, q, cu, [0, 8])
+    with pytest.raises(TypeError, match="torch.Tensor"):
+        fa.observe_amax(None, q, q, q)
+    with pytest.raises(TypeError, match="torch.Tensor"):
+        fa.scales(None, "dynamic")

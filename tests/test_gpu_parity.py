@@ -356,6 +356,37 @@ def test_two_layers_on_two_streams_concurrently():
     assert torch.equal(seq_sa, con_sa) and torch.equal(seq_sb, con_sb)
 
 
+def test_binding_rejects_bad_arguments_on_the_host():
+    # each call fails in the binding or in the C-ABI's host checks, before any launch
+    T, H = 64, 2
+    qkv = torch.randn(T, 3, H, 128, device=DEV).to(torch.bfloat16)   # a fused projection
+    q, k, v = (qkv[:, i].contiguous() for i in range(3))
+    cu = [0, T]
+    cu_d = _cu_dev(cu)
+    layer = fa.AttentionLayer(DEV)
+    say("binding argument checks")
+    with pytest.raises(ValueError, match="contiguous"):
+        fa.forward(layer.state, qkv[:, 0], k, v, cu_d, cu)
+    with pytest.raises(TypeError, match="bfloat16"):
+        fa.forward(layer.state, q.half(), k, v, cu_d, cu)
+    with pytest.raises(ValueError, match="shapes differ"):
+        fa.forward(layer.state, q, k[:32], v, cu_d, cu)
+    with pytest.raises(ValueError, match="tokens"):
+        fa.forward(layer.state, q, k, v, _cu_dev([0, T - 1]), [0, T - 1])
+    with pytest.raises(ValueError, match="state must hold"):
+        fa.forward(torch.zeros(100, dtype=torch.uint8, device=DEV), q, k, v, cu_d, cu)
+    with pytest.raises(ValueError, match="state must hold"):
+        fa.quantize(torch.zeros(100, dtype=torch.uint8, device=DEV), q, k, v, cu_d, cu)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        fa.quantize(torch.zeros(1280, dtype=torch.uint8), q, k, v, cu_d, cu)
+    q64 = torch.zeros(T, H, 64, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(_lib.Fp8AttnError) as ei:
+        fa.forward(layer.state, q64, q64, q64, cu_d, cu)
+    assert ei.value.code == -2
+    torch.cuda.synchronize()
+    assert int(torch.count_nonzero(layer.state)) == 0     # nothing ran on the state
+
+
 def test_nonpositive_softmax_scale_selects_the_default():
     # softmax_scale <= 0 means 1/sqrt(head_dim): bit-identical to passing that value
     q, k, v, cu = random_varlen([200, 77], 2, seed=92, device=DEV)
