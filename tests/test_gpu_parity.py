@@ -199,6 +199,16 @@ def test_quantize_saturates_static():
     _check_workspace(ws, q, k, v, cu, sc)
     q8 = fa.split_workspace(ws, q.shape[0], 2, 2)[0].to("cpu").numpy()
     assert np.sum((q8 & 0x7F) == 0x7E) > 10
+    # attention on the saturated codes: the oracle saturates the same elements
+    out = fa.attend(st, ws, _cu_dev(cu), cu, 2)
+    torch.cuda.synchronize()
+    got, want = bf16_to_f64(out), oracle_fp8_rows(q, k, v, cu, sc, SM)
+    luts = [quant_lut(x[1]) for x in sc]
+    bound = hw_bound_rows(luts[0][bits(q)], luts[1][bits(k)], luts[2][bits(v)], cu, sc, SM,
+                          np.arange(q.shape[0]))
+    stats = check_rows(got, want, bound, v_channel_std(v)[None])
+    say(f"  attention on saturated codes: {stats}")
+    assert stats["ok"], stats
 
 
 @pytest.mark.parametrize("amax", [1.0, 448.0, 3.0e38, 1e-20, 0.0, 2.5e-6])
