@@ -12,7 +12,10 @@ heads, head_dim 128, bf16 N(0,1) with x20 outlier columns).
 
 Prints ONE JSON line. value = attention FLOPs of the step (4 * S^2 * d * H) / step time,
 in TFLOP/s, the step time being the wall time of K back-to-back steps between two device
-synchronisations. Before them, an untimed warm-up of at least W steps and at least
+synchronisations. The timed steps replay a HIP graph of one step (its four kernel launches
+captured once), so that the Python side of the launches, which on a slow host can take
+longer than the kernels, stays out of the figure; the same K steps launched one by one from
+Python are reported beside it (ms_per_step_eager_launches). Before them, an untimed warm-up of at least W steps and at least
 --settle-ms of continuous work: after an idle stretch the GPU's clock ramps up over the
 first tens of milliseconds of work (at the kernel point a step averages about 450 us over
 its first 20 runs and settles near 325 us after about 50 ms), and the benchmark reports the
@@ -325,6 +328,38 @@ def regime(fa, dev, settle_ms=60.0):
     return rows
 
 
+def dit_schedule_time(fa, dev):
+    """The DiT workload's whole schedule: 4 denoising steps x 8 layers of one 57 600-token,
+    40-head full-attention forward, the step and layer skip selectors (steps 0,1 and layers
+    0-2, vLLM-Omni "Quantized KV Cache", "Parameters") routing 22 of the 32 forwards to the
+    BF16 kernel and the rest through each layer's dynamic FP8 path; against all 32 in BF16.
+    One set of inputs serves every forward (the times do not depend on the values)."""
+    import torch
+    from workloads import WORKLOADS, dit_schedule, make_qkv
+    w = WORKLOADS["dit"]
+    q, k, v = make_qkv(w, 0, dev)
+    cu = list(w.cu_seqlens)
+    cu_d = torch.tensor(cu, dtype=torch.int32, device=dev)
+    out = torch.empty_like(q)
+    layers = [fa.AttentionLayer(dev) for _ in range(w.layers)]
+    sched = dit_schedule(w, fa.parse_selector(w.skip_steps), fa.parse_selector(w.skip_layers))
+
+    def run(all_bf16):
+        for (_, _, layer, skip) in sched:
+            layers[layer](q, k, v, cu_d, cu, skip=skip or all_bf16, out=out)
+
+    settle([lambda: run(False)], 1, 0.0)
+    t_mixed = _burst_ms(lambda: run(False), 1)
+    t_bf16 = _burst_ms(lambda: run(True), 1)
+    n_bf16 = sum(1 for x in sched if x[3])
+    res = {"forwards": len(sched), "bf16_forwards": n_bf16, "fp8_forwards": len(sched) - n_bf16,
+           "schedule_ms": round(t_mixed, 2), "all_bf16_ms": round(t_bf16, 2),
+           "speedup": round(t_bf16 / t_mixed, 3)}
+    del q, k, v, out, layers
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -369,10 +404,26 @@ def main():
         ev[3].record()
 
     warm_rounds = settle([step], args.warmup, args.settle_ms)
+    # the same steps launched one by one from Python, for reference: on a slow host the
+    # Python side of two binding calls and four launches can take longer than the kernels
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step()
+    torch.cuda.synchronize()
+    ms_step_eager = (time.perf_counter() - t0) * 1e3 / args.steps
+
+    # the timed steps: one step captured in a HIP graph (observe-quantise, scales,
+    # re-quantise check, attention; no allocation, copy or memset inside) and replayed K
+    # times, so the launches come from the graph and the host's speed stays out of the step
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    settle([graph.replay], 1, 50.0)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        graph.replay()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
@@ -446,13 +497,15 @@ def main():
         "warmup_steps_run": warm_rounds,
         "settle_ms": args.settle_ms,
         "ms_per_step": round(ms_step, 4),
+        "ms_per_step_eager_launches": round(ms_step_eager, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp8_e4m3 (fp32 accumulate)",
         "data": f"synthetic (seeded bf16; {w.description.split(';')[0].split(', ', 2)[-1]})",
         "config": {"workload": f"{w.name}: {w.description}", "num_seqs": B, "seq_len": w.seq_lens[0],
-                   "num_heads": H, "head_dim": D, "causal": False, "scaling": "dynamic 16-slot ring"},
+                   "num_heads": H, "head_dim": D, "causal": False, "scaling": "dynamic 16-slot ring",
+                   "launch": "one step captured in a HIP graph, replayed per timed step"},
         "roofline": {"bound": "mfma", "kernel": "attn_fp8_kernel",
                      "achieved": round(attn_tflops, 2), "peak": FP8_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / FP8_PEAK_TFLOPS, 4),
@@ -492,6 +545,7 @@ def main():
             "scaling, window maximum steady), attn_bf16 = the skip-path kernel; 3 images "
             "per request unless the name says x N, 16-pixel patches, H=16 (DiT: one "
             "forward, H=40)")
+        result["dit_schedule"] = dit_schedule_time(fa, dev)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, q, k, v, cu, args.cpu_rows)
     if args.copy_calibration_mib > 0:
