@@ -39,6 +39,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -163,7 +165,7 @@ def cold_quant(fa, w, q, k, v, cu_d, cu, st, ws, dev, reps=10):
     del flush
     w4 = WORKLOADS["4k"]
     q4, k4, v4 = make_qkv(w4, 0, dev)
-    cu4 = list(w4.cu_seqlens)
+    cu4 = np.asarray(w4.cu_seqlens, dtype=np.int32)
     cu4_d = torch.tensor(cu4, dtype=torch.int32, device=dev)
     st4 = fa.new_state(dev)
     ws4 = torch.empty(fa.workspace_bytes(w4.total_tokens, w4.num_seqs, w4.num_heads,
@@ -294,7 +296,7 @@ def regime(fa, dev, settle_ms=60.0):
                   Workload("dit-shard", 5, (0, 57600), 10, outliers=True)))
     for name, w in cases:
         q, k, v = make_qkv(w, 0, dev)
-        cu = list(w.cu_seqlens)
+        cu = np.asarray(w.cu_seqlens, dtype=np.int32)
         cu_d = torch.tensor(cu, dtype=torch.int32, device=dev)
         H = w.num_heads
         st = fa.new_state(dev)
@@ -338,7 +340,7 @@ def dit_schedule_time(fa, dev):
     from workloads import WORKLOADS, dit_schedule, make_qkv
     w = WORKLOADS["dit"]
     q, k, v = make_qkv(w, 0, dev)
-    cu = list(w.cu_seqlens)
+    cu = np.asarray(w.cu_seqlens, dtype=np.int32)
     cu_d = torch.tensor(cu, dtype=torch.int32, device=dev)
     out = torch.empty_like(q)
     layers = [fa.AttentionLayer(dev) for _ in range(w.layers)]
@@ -375,7 +377,7 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     q, k, v = make_qkv(w, 0, dev)
-    cu = list(w.cu_seqlens)
+    cu = np.asarray(w.cu_seqlens, dtype=np.int32)
     cu_d = torch.tensor(cu, dtype=torch.int32, device=dev)
     B, H, D, T = w.num_seqs, w.num_heads, w.head_dim, w.total_tokens
     st = fa.new_state(dev)
