@@ -20,6 +20,9 @@ FP8ATTN_OBSERVE = 2
 
 _c_void_p = ctypes.c_void_p
 _i32p = ctypes.POINTER(ctypes.c_int32)
+# host int32 tables (cu_seqlens_host) are passed by address as void pointers: the same ABI
+# as const int32_t*, and an integer address avoids building a typed pointer per call
+_host_i32 = ctypes.c_void_p
 _f32p = ctypes.POINTER(ctypes.c_float)
 
 # name -> (restype, argtypes); every function declared in include/fp8attn.h
@@ -33,17 +36,17 @@ SIGNATURES = {
     "fp8attn_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int, ctypes.c_int,
                                                   ctypes.c_int]),
     "fp8attn_quantize": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
-                                        _i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                        _host_i32, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                         _c_void_p, ctypes.c_size_t, _c_void_p]),
     "fp8attn_quantize_dynamic": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p,
-                                                _c_void_p, _i32p, ctypes.c_int, ctypes.c_int,
+                                                _c_void_p, _host_i32, ctypes.c_int, ctypes.c_int,
                                                 ctypes.c_int, _c_void_p, ctypes.c_size_t,
                                                 _c_void_p]),
     "fp8attn_forward": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
-                                       _i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                       _host_i32, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                        ctypes.c_float, ctypes.c_uint, _c_void_p,
                                        ctypes.c_size_t, _c_void_p, _c_void_p]),
-    "fp8attn_attend": (ctypes.c_int, [_c_void_p, _c_void_p, _i32p, ctypes.c_int, ctypes.c_int,
+    "fp8attn_attend": (ctypes.c_int, [_c_void_p, _c_void_p, _host_i32, ctypes.c_int, ctypes.c_int,
                                       ctypes.c_int, ctypes.c_float, _c_void_p, ctypes.c_size_t,
                                       _c_void_p, _c_void_p]),
     "fp8attn_last_error": (ctypes.c_char_p, []),

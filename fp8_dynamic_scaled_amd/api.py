@@ -29,6 +29,11 @@ def _stream(device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+def _host_addr(a: np.ndarray) -> int:
+    """Address of a host int32 table (the caller keeps the array alive for the call)."""
+    return a.__array_interface__["data"][0]
+
+
 def _ptr(t: Optional[torch.Tensor]) -> ctypes.c_void_p:
     return ctypes.c_void_p(0 if t is None else t.data_ptr())
 
@@ -149,7 +154,7 @@ def quantize(state, q, k, v, cu_seqlens, cu_seqlens_host=None,
     _need_cuda("workspace", workspace, torch.uint8)
     check("fp8attn_quantize",
           _lib.load().fp8attn_quantize(_ptr(state), _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens),
-                                       host.ctypes.data_as(_lib._i32p), B, H, D, _ptr(workspace),
+                                       _host_addr(host), B, H, D, _ptr(workspace),
                                        workspace.numel(), _stream(q.device)))
     return workspace
 
@@ -168,7 +173,7 @@ def quantize_dynamic(state, q, k, v, cu_seqlens, cu_seqlens_host=None,
     _need_cuda("workspace", workspace, torch.uint8)
     check("fp8attn_quantize_dynamic",
           _lib.load().fp8attn_quantize_dynamic(_ptr(state), _ptr(q), _ptr(k), _ptr(v),
-                                               _ptr(cu_seqlens), host.ctypes.data_as(_lib._i32p),
+                                               _ptr(cu_seqlens), _host_addr(host),
                                                B, H, D, _ptr(workspace), workspace.numel(),
                                                _stream(q.device)))
     return workspace
@@ -205,7 +210,7 @@ def attend(state, workspace, cu_seqlens, cu_seqlens_host, num_heads: int,
     if tuple(out.shape) != (T, num_heads, head_dim):
         raise ValueError("out must be [total_tokens, num_heads, head_dim]")
     check("fp8attn_attend",
-          _lib.load().fp8attn_attend(_ptr(state), _ptr(cu_seqlens), host.ctypes.data_as(_lib._i32p),
+          _lib.load().fp8attn_attend(_ptr(state), _ptr(cu_seqlens), _host_addr(host),
                                      B, num_heads, head_dim, ctypes.c_float(softmax_scale),
                                      _ptr(workspace), workspace.numel(), _ptr(out),
                                      _stream(workspace.device)))
@@ -240,7 +245,7 @@ def forward(state, q, k, v, cu_seqlens, cu_seqlens_host=None, softmax_scale: flo
     flags = (FP8ATTN_SKIP if skip else 0) | (FP8ATTN_OBSERVE if observe else 0)
     check("fp8attn_forward",
           _lib.load().fp8attn_forward(_ptr(state), _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens),
-                                      host.ctypes.data_as(_lib._i32p), B, H, D,
+                                      _host_addr(host), B, H, D,
                                       ctypes.c_float(softmax_scale), flags,
                                       _ptr(workspace if not skip else None), ws_n, _ptr(out),
                                       _stream(q.device)))
