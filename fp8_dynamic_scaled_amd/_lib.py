@@ -49,6 +49,10 @@ SIGNATURES = {
     "fp8attn_attend": (ctypes.c_int, [_c_void_p, _c_void_p, _host_i32, ctypes.c_int, ctypes.c_int,
                                       ctypes.c_int, ctypes.c_float, _c_void_p, ctypes.c_size_t,
                                       _c_void_p, _c_void_p]),
+    "fp8attn_forward_noalloc": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                               _c_void_p, _host_i32, ctypes.c_int, ctypes.c_int,
+                                               ctypes.c_int, ctypes.c_float, ctypes.c_uint,
+                                               _c_void_p, _c_void_p]),
     "fp8attn_last_error": (ctypes.c_char_p, []),
 }
 

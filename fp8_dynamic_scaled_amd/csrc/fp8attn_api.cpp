@@ -10,6 +10,7 @@
 #include <string>
 
 #include "fp8attn.h"
+#include "api_internal.h"
 #include "launch.h"
 
 static_assert(sizeof(fp8attn_state) == 1280, "fp8attn_state is part of the ABI");
@@ -96,6 +97,90 @@ int check_varlen(const char* fn, const void* q, const void* k, const void* v,
 }
 
 }  // namespace
+
+namespace fp8attn {
+
+int hip_result(hipError_t e, const char* what) { return hip_status(e, what); }
+
+int forward_impl(const char* fn, void* state, const void* q, const void* k, const void* v,
+                 const int32_t* cu_seqlens, const int32_t* cu_seqlens_host, int num_seqs,
+                 int num_heads, int head_dim, float softmax_scale, unsigned flags,
+                 void* workspace, size_t workspace_bytes, void* out, void* stream,
+                 int (*acquire_scratch)(void** workspace)) {
+  const bool scratch = acquire_scratch != nullptr;
+  if (flags & ~(FP8ATTN_SKIP | FP8ATTN_OBSERVE))
+    return fail(FP8ATTN_EINVAL, "%s: unknown flag bits 0x%x", fn, flags);
+  if ((flags & FP8ATTN_SKIP) && (flags & FP8ATTN_OBSERVE))
+    return fail(FP8ATTN_EINVAL, "%s: FP8ATTN_OBSERVE and FP8ATTN_SKIP exclude each other", fn);
+  Varlen vl;
+  int rc = check_varlen(fn, q, k, v, cu_seqlens, cu_seqlens_host, num_seqs, num_heads, head_dim, &vl);
+  if (rc != FP8ATTN_OK) return rc;
+  if ((vl.T > 0 && !out) || !aligned16(out))
+    return fail(FP8ATTN_EINVAL, "%s: out must be non-NULL and 16-byte aligned", fn);
+  if (!std::isfinite(softmax_scale))
+    return fail(FP8ATTN_EINVAL, "%s: softmax_scale must be finite", fn);
+  const bool skip = (flags & FP8ATTN_SKIP) != 0;
+  // the BF16 kernel addresses one sequence of a bf16 tensor with 32-bit byte offsets
+  if (skip && (int64_t)vl.max_seqlen * num_heads * head_dim * 2 > ((int64_t)1 << 31) - 1)
+    return fail(FP8ATTN_EUNSUPPORTED,
+                "%s: the BF16 path needs longest sequence x num_heads x head_dim x 2 bytes < 2^31", fn);
+  if (!skip) {
+    if (!state) return fail(FP8ATTN_EINVAL, "%s: the FP8 path needs a state", fn);
+    if (scratch && workspace_bytes < vl.ws_bytes)
+      return fail(FP8ATTN_EINVAL,
+                  "%s: this call needs %zu bytes of workspace; the library's fixed scratch "
+                  "holds %zu", fn, vl.ws_bytes, workspace_bytes);
+    // every argument is checked: only now look up the fixed scratch array
+    if (scratch && (rc = acquire_scratch(&workspace)) != FP8ATTN_OK) return rc;
+    if (!workspace || !aligned16(workspace))
+      return fail(FP8ATTN_EINVAL, "%s: workspace must be non-NULL and 16-byte aligned", fn);
+    if (workspace_bytes < vl.ws_bytes)
+      return fail(FP8ATTN_EINVAL, "%s: workspace of %zu bytes is smaller than the %zu needed",
+                  fn, workspace_bytes, vl.ws_bytes);
+  }
+  const bool observe = (flags & FP8ATTN_OBSERVE) != 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (vl.T == 0) {
+    if (!observe) return ok();
+    return hip_status(fp8attn::launch_scales(static_cast<fp8attn_state*>(state), FP8ATTN_DYNAMIC,
+                                             nullptr, 0.0f, s),
+                      fn);
+  }
+  const float sm = softmax_scale > 0.0f ? softmax_scale
+                                        : (float)(1.0 / std::sqrt((double)head_dim));
+  fp8attn::AttnLaunch a;
+  a.cu = cu_seqlens;
+  a.num_seqs = num_seqs;
+  a.H = num_heads;
+  a.T = vl.T;
+  a.Tp = vl.Tp;
+  a.max_seqlen = vl.max_seqlen;
+  a.softmax_scale = sm;
+  a.out = static_cast<uint16_t*>(out);
+  if (skip) {
+    return hip_status(fp8attn::launch_attn_bf16(a, static_cast<const uint16_t*>(q),
+                                                static_cast<const uint16_t*>(k),
+                                                static_cast<const uint16_t*>(v), s),
+                      fn);
+  }
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  const int64_t n = vl.T * num_heads * head_dim;
+  const fp8attn_state* st = static_cast<const fp8attn_state*>(state);
+  const uint16_t* q16 = static_cast<const uint16_t*>(q);
+  const uint16_t* k16 = static_cast<const uint16_t*>(k);
+  const uint16_t* v16 = static_cast<const uint16_t*>(v);
+  hipError_t e =
+      observe ? fp8attn::launch_quantize_dynamic(static_cast<fp8attn_state*>(state), q16, k16, v16,
+                                                 cu_seqlens, num_seqs, vl.T, num_heads, ws,
+                                                 ws + n, ws + 2 * n, vl.Tp, s)
+              : fp8attn::launch_quantize(st, q16, k16, v16, cu_seqlens, num_seqs, vl.T,
+                                         num_heads, ws, ws + n, ws + 2 * n, vl.Tp, s);
+  if (e != hipSuccess) return hip_status(e, fn);
+  return hip_status(fp8attn::launch_attn_fp8(a, st, ws, ws + n, ws + 2 * n, s),
+                    fn);
+}
+
+}  // namespace fp8attn
 
 extern "C" {
 
@@ -253,71 +338,10 @@ int fp8attn_forward(void* state, const void* q, const void* k, const void* v,
                     const int32_t* cu_seqlens, const int32_t* cu_seqlens_host, int num_seqs,
                     int num_heads, int head_dim, float softmax_scale, unsigned flags,
                     void* workspace, size_t workspace_bytes, void* out, void* stream) {
-  const char* fn = "fp8attn_forward";
-  if (flags & ~(FP8ATTN_SKIP | FP8ATTN_OBSERVE))
-    return fail(FP8ATTN_EINVAL, "%s: unknown flag bits 0x%x", fn, flags);
-  if ((flags & FP8ATTN_SKIP) && (flags & FP8ATTN_OBSERVE))
-    return fail(FP8ATTN_EINVAL, "%s: FP8ATTN_OBSERVE and FP8ATTN_SKIP exclude each other", fn);
-  Varlen vl;
-  int rc = check_varlen(fn, q, k, v, cu_seqlens, cu_seqlens_host, num_seqs, num_heads, head_dim, &vl);
-  if (rc != FP8ATTN_OK) return rc;
-  if ((vl.T > 0 && !out) || !aligned16(out))
-    return fail(FP8ATTN_EINVAL, "%s: out must be non-NULL and 16-byte aligned", fn);
-  if (!std::isfinite(softmax_scale))
-    return fail(FP8ATTN_EINVAL, "%s: softmax_scale must be finite", fn);
-  const bool skip = (flags & FP8ATTN_SKIP) != 0;
-  // the BF16 kernel addresses one sequence of a bf16 tensor with 32-bit byte offsets
-  if (skip && (int64_t)vl.max_seqlen * num_heads * head_dim * 2 > ((int64_t)1 << 31) - 1)
-    return fail(FP8ATTN_EUNSUPPORTED,
-                "%s: the BF16 path needs longest sequence x num_heads x head_dim x 2 bytes < 2^31", fn);
-  if (!skip) {
-    if (!state) return fail(FP8ATTN_EINVAL, "%s: the FP8 path needs a state", fn);
-    if (!workspace || !aligned16(workspace))
-      return fail(FP8ATTN_EINVAL, "%s: workspace must be non-NULL and 16-byte aligned", fn);
-    if (workspace_bytes < vl.ws_bytes)
-      return fail(FP8ATTN_EINVAL, "%s: workspace of %zu bytes is smaller than the %zu needed",
-                  fn, workspace_bytes, vl.ws_bytes);
-  }
-  const bool observe = (flags & FP8ATTN_OBSERVE) != 0;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (vl.T == 0) {
-    if (!observe) return ok();
-    return hip_status(fp8attn::launch_scales(static_cast<fp8attn_state*>(state), FP8ATTN_DYNAMIC,
-                                             nullptr, 0.0f, s),
-                      fn);
-  }
-  const float sm = softmax_scale > 0.0f ? softmax_scale
-                                        : (float)(1.0 / std::sqrt((double)head_dim));
-  fp8attn::AttnLaunch a;
-  a.cu = cu_seqlens;
-  a.num_seqs = num_seqs;
-  a.H = num_heads;
-  a.T = vl.T;
-  a.Tp = vl.Tp;
-  a.max_seqlen = vl.max_seqlen;
-  a.softmax_scale = sm;
-  a.out = static_cast<uint16_t*>(out);
-  if (skip) {
-    return hip_status(fp8attn::launch_attn_bf16(a, static_cast<const uint16_t*>(q),
-                                                static_cast<const uint16_t*>(k),
-                                                static_cast<const uint16_t*>(v), s),
-                      fn);
-  }
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
-  const int64_t n = vl.T * num_heads * head_dim;
-  const fp8attn_state* st = static_cast<const fp8attn_state*>(state);
-  const uint16_t* q16 = static_cast<const uint16_t*>(q);
-  const uint16_t* k16 = static_cast<const uint16_t*>(k);
-  const uint16_t* v16 = static_cast<const uint16_t*>(v);
-  hipError_t e =
-      observe ? fp8attn::launch_quantize_dynamic(static_cast<fp8attn_state*>(state), q16, k16, v16,
-                                                 cu_seqlens, num_seqs, vl.T, num_heads, ws,
-                                                 ws + n, ws + 2 * n, vl.Tp, s)
-              : fp8attn::launch_quantize(st, q16, k16, v16, cu_seqlens, num_seqs, vl.T,
-                                         num_heads, ws, ws + n, ws + 2 * n, vl.Tp, s);
-  if (e != hipSuccess) return hip_status(e, "fp8attn_forward (quantise)");
-  return hip_status(fp8attn::launch_attn_fp8(a, st, ws, ws + n, ws + 2 * n, s),
-                    "fp8attn_forward (attention)");
+  return fp8attn::forward_impl("fp8attn_forward", state, q, k, v, cu_seqlens, cu_seqlens_host,
+                               num_seqs, num_heads, head_dim,
+                               softmax_scale, flags, workspace, workspace_bytes, out, stream,
+                               nullptr);
 }
 
 }  // extern "C"

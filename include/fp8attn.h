@@ -29,7 +29,7 @@
  *     only enqueues work on that stream and never waits for the device.
  *   - The caller owns every buffer (state, workspace, inputs, outputs). The library
  *     allocates no device memory and keeps no global state apart from the thread-local
- *     error message.
+ *     error message and the fixed scratch array of fp8attn_forward_noalloc.
  *   - Argument checks happen on the host before anything is enqueued. A failed check
  *     returns a negative status, enqueues nothing, and sets fp8attn_last_error().
  *     A failed kernel launch returns FP8ATTN_EHIP.
@@ -239,6 +239,30 @@ int fp8attn_forward(void* state, const void* q, const void* k, const void* v,
                     const int32_t* cu_seqlens, const int32_t* cu_seqlens_host, int num_seqs,
                     int num_heads, int head_dim, float softmax_scale, unsigned flags,
                     void* workspace, size_t workspace_bytes, void* out, void* stream);
+
+/*
+ * For callers that cannot allocate device memory: code under HIP graph capture, serving
+ * loops and harnesses that forbid hipMalloc. The same call as fp8attn_forward, without the
+ * workspace argument: the FP8 path's workspace is a fixed device array inside the library,
+ * FP8ATTN_NOALLOC_SCRATCH_BYTES long (64 MiB: up to 10 880 tokens at 16 heads), one
+ * per GPU, held from the library's first use on that GPU until the process ends. The call
+ * allocates nothing; on its first use on a device it looks up that device's array address
+ * (hipGetSymbolAddress) with that device current. The device that is current during the
+ * call must be the stream's device.
+ * Concurrency: all calls on one GPU share its array, so calls that overlap in time on one
+ * GPU (two streams, two host threads) race on it and must be serialised by the caller.
+ * Nothing in the array needs to start at zero; a call's results do not depend on what an
+ * earlier call left there.
+ * Errors: as fp8attn_forward; EINVAL (before anything is enqueued) when the FP8 path would
+ * need more than FP8ATTN_NOALLOC_SCRATCH_BYTES, i.e. when fp8attn_workspace_bytes(total
+ * tokens, num_seqs, num_heads, head_dim) exceeds it; EHIP when the array's address cannot
+ * be obtained. The BF16 path (FP8ATTN_SKIP) does not touch the array.
+ */
+#define FP8ATTN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int fp8attn_forward_noalloc(void* state, const void* q, const void* k, const void* v,
+                            const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+                            int num_seqs, int num_heads, int head_dim, float softmax_scale,
+                            unsigned flags, void* out, void* stream);
 
 /* Message describing the last non-OK return on the calling thread ("" if none). */
 const char* fp8attn_last_error(void);

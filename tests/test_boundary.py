@@ -33,7 +33,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     for name in names:
         assert hasattr(lib, name), name
         assert name in _lib.SIGNATURES, name
@@ -207,3 +207,33 @@ def test_binding_rejects_host_tensors_before_any_gpu_call():
         fa.observe_amax(None, q, q, q)
     with pytest.raises(TypeError, match="torch.Tensor"):
         fa.scales(None, "dynamic")
+
+
+def _fwd_noalloc(lib, **kw):
+    a = dict(state=P, q=P, k=P, v=P, cu=P, cu_host=_cu([0, 8, 16]), num_seqs=2, H=2, D=128,
+             sm=0.0, flags=0, out=P, stream=NULL)
+    a.update(kw)
+    return lib.fp8attn_forward_noalloc(a["state"], a["q"], a["k"], a["v"], a["cu"],
+                                       a["cu_host"], a["num_seqs"], a["H"], a["D"],
+                                       ctypes.c_float(a["sm"]), a["flags"], a["out"],
+                                       a["stream"])
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(q=NULL), -1, "non-NULL"),
+    (dict(cu_host=None), -1, "cu_seqlens"),
+    (dict(D=64), -2, "head_dim"),
+    (dict(flags=3), -1, "exclude each other"),
+    (dict(state=NULL), -1, "state"),
+    (dict(out=NULL), -1, "out"),
+    # one sequence of 10 881 tokens x 16 heads needs more workspace than the fixed scratch
+    # (10 880 fill it exactly)
+    (dict(cu_host=_cu([0, 10881]), num_seqs=1, H=16), -1, "fixed scratch"),
+])
+def test_forward_noalloc_rejects_before_any_hip_call(lib, kw, code, needle):
+    # every argument, the workspace size included, is checked before the library looks up
+    # its scratch array, so these fail the same way without a device
+    assert _fwd_noalloc(lib, **kw) == code
+    assert needle in lib.fp8attn_last_error().decode()
+    assert lib.fp8attn_workspace_bytes(10881, 1, 16, 128) > (64 << 20)
+    assert lib.fp8attn_workspace_bytes(10880, 1, 16, 128) == (64 << 20)
