@@ -104,7 +104,7 @@ def cpu_baseline(w, q, k, v, cu, rows_per_head):
     sm = float(np.float32(1.0 / math.sqrt(w.head_dim)))
     t1 = time.perf_counter()
     oracle.fp8_attention(codes[0], codes[1], codes[2], list(cu), sc[0][0], sc[1][0], sc[2][0],
-                         sm, tokens=toks, kv_block=64)
+                         sm, tokens=toks)
     t_attn = time.perf_counter() - t1
     frac = rows_per_head / w.total_tokens
     t_full = t_quant + t_attn / frac

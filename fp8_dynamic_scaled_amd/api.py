@@ -17,7 +17,6 @@ from ._lib import FP8ATTN_DYNAMIC, FP8ATTN_OBSERVE, FP8ATTN_SKIP, FP8ATTN_STATIC
 
 HEAD_DIM = 128
 DEFAULT_MARGIN = 1.5
-KV_BLOCK = 64          # FP8ATTN_KV_BLOCK: keys per online-softmax block of the FP8 path
 CUR_STRIPES = 16       # FP8ATTN_CUR_STRIPES
 STATE_DTYPE = np.dtype([("ring", "<f4", (3, 16)), ("count", "<u4"),
                         ("scale", "<f4", (3,)), ("inv_scale", "<f4", (3,)),

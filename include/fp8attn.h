@@ -67,9 +67,6 @@ typedef enum fp8attn_status {
                               instead of the state's current scales; excludes SKIP */
 
 #define FP8ATTN_RING_SLOTS 16
-/* Keys per online-softmax block of the FP8 path: P is quantised to E4M3 relative to the
- * running row maximum of the blocks of 64 keys seen so far (sequence order). */
-#define FP8ATTN_KV_BLOCK 64
 #define FP8ATTN_E4M3_MAX 448.0f
 #define FP8ATTN_DEFAULT_MARGIN 1.5f
 
@@ -213,11 +210,11 @@ int fp8attn_attend(const void* state, const int32_t* cu_seqlens, const int32_t* 
  *   O[r,h,:] = sum_j w_j V[j,h,:] over the keys j of sequence i only.
  * FP8 path (flags without FP8ATTN_SKIP): quantises Q, K, V with the state's scales into
  *   `workspace` (see fp8attn_workspace_bytes), then s_j = (q8.k8_j) * scale_q * scale_k *
- *   softmax_scale, and an online softmax over blocks of FP8ATTN_KV_BLOCK keys: with m the
- *   running row maximum after the current block, p8_j = E4M3(exp(s_j - m) * 448) (fixed
- *   scale 448, so p8_j <= 448); earlier sums are rescaled by exp(m_old - m) when m grows;
- *   O = scale_v * sum_j p8'_j v8_j / sum_j p8'_j with p8' the rescaled weights. The PV
- *   product uses the E4M3 V; accumulation and softmax are fp32; O is bf16.
+ *   softmax_scale; with m = max_j s_j, the row maximum over all keys of the sequence,
+ *   p8_j = E4M3(exp(s_j - m) * 448) (fixed scale 448, so p8_j <= 448); O = scale_v *
+ *   sum_j p8_j v8_j / sum_j p8_j. The PV product uses the E4M3 V; accumulation and softmax
+ *   are fp32 (the scores and products on FP8 matrix cores); O is bf16. The result does not
+ *   depend on how the kernel tiles the keys.
  *   Requires a preceding fp8attn_scales on this state (same stream), unless
  *   FP8ATTN_OBSERVE is set: then the call itself performs the dynamic observe + ring +
  *   scales update (fp8attn_quantize_dynamic) before the attention, writing the state.

@@ -12,22 +12,13 @@ The pages print no formula, so the attention is the textbook definition applied 
 packed sequence (block-diagonal, non-causal), with these readings:
   * softmax scale sigma is an explicit argument (1/sqrt(d) by default);
   * scores use the dequantised E4M3 operands: s_j = (q8 . k8_j) * scale_q * scale_k * sigma;
-  * P is quantised with the fixed scale 448 relative to a row maximum m, so that
-    P~_j = exp(s_j - m) lies in (0, 1] and p8_j = E4M3(P~_j * 448);
+  * P is quantised with the fixed scale 448 relative to the row maximum m = max_j s_j over
+    all keys of the row's sequence, so that P~_j = exp(s_j - m) lies in (0, 1] and
+    p8_j = E4M3(P~_j * 448);
   * the weights are the quantised p8_j normalised by their own sum (rows of weights sum
     to 1 and a constant V comes out unchanged); O is multiplied by scale_v.
-Which maximum m: the backends the pages name are FP8 *flash* attentions (vLLM docs,
-"FP8 ViT Encoder Attention": the core FP8 flash-attention kernel in "Performance"; Korean
-wiki "Requirements": a varlen FP8 flash attention), i.e. an online softmax over blocks of
-keys in which P is cast to FP8 inside the loop, relative to the running maximum of the
-blocks seen so far. Two readings are implemented:
-  * kv_block = B (the online-softmax rule, the one the GPU path follows with B = 64):
-    keys are visited in blocks of B in sequence order; for each block, m_new = max(m,
-    block max), the accumulated L and O are multiplied by exp(m - m_new), then
-    p8_j = E4M3(exp(s_j - m_new) * 448) for the block's keys, L += sum dec(p8_j) and
-    O += sum dec(p8_j) dec(v8_j); finally O * scale_v / L;
-  * kv_block = None: m is the global row maximum over all keys (one block).
-The two agree exactly whenever the first block holds the row maximum.
+The maximum is the row's own, over every key: no page fixes a block of keys, so how an
+implementation tiles the keys is not part of the result.
 Exactness: E4M3 values are multiples of 2^-9 below 2^9, so every product is a multiple
 of 2^-18 below 2^18; the d = 128 score sum stays below 2^43 units and the PV sum over
 up to ~2^17 keys below 2^53 units -- both are exact in float64 whatever the summation
@@ -45,17 +36,11 @@ _ROW_GROUP = 512
 
 
 def fp8_attention_head(q8, k8, v8, scale_q, scale_k, scale_v, sm_scale,
-                       return_weights=False, kv_block=None):
+                       return_weights=False):
     """One (sequence, head): q8 [R, d], k8 [S, d], v8 [S, d] E4M3 codes -> O [R, d].
 
-    kv_block=None: global row maximum; kv_block=B: online softmax over blocks of B keys.
-    With return_weights=True also returns, for the global maximum, the p8 codes [R, S] and
-    L [R]; for the online rule, the effective weights [R, S] (each block's dec(p8) times
-    the later rescale factors, over the final L) and L [R].
+    With return_weights=True also returns the p8 codes [R, S] and L [R].
     """
-    if kv_block is not None:
-        return _fp8_attention_head_online(q8, k8, v8, scale_q, scale_k, scale_v, sm_scale,
-                                          int(kv_block), return_weights)
     q = e4m3_decode(q8)
     k = e4m3_decode(k8)
     v = e4m3_decode(v8)
@@ -82,50 +67,6 @@ def fp8_attention_head(q8, k8, v8, scale_q, scale_k, scale_v, sm_scale,
             all_L[r0:r1] = L
     if return_weights:
         return out, all_p8, all_L
-    return out
-
-
-def _fp8_attention_head_online(q8, k8, v8, scale_q, scale_k, scale_v, sm_scale, block,
-                               return_weights):
-    """Online-softmax rule: P quantised relative to the running maximum of key blocks."""
-    q = e4m3_decode(q8)
-    k = e4m3_decode(k8)
-    v = e4m3_decode(v8)
-    c = float(scale_q) * float(scale_k) * float(sm_scale)
-    R, d = q.shape
-    S = k.shape[0]
-    out = np.zeros((R, d), dtype=np.float64)
-    weights = np.zeros((R, S)) if return_weights else None
-    L_all = np.zeros(R) if return_weights else None
-    if S == 0:
-        return (out, weights, L_all) if return_weights else out
-    for r0 in range(0, R, _ROW_GROUP):
-        r1 = min(R, r0 + _ROW_GROUP)
-        rows = r1 - r0
-        m = np.full(rows, -np.inf)
-        L = np.zeros(rows)
-        acc = np.zeros((rows, d))
-        w = np.zeros((rows, S)) if return_weights else None
-        for j0 in range(0, S, block):
-            j1 = min(S, j0 + block)
-            s = (q[r0:r1] @ k[j0:j1].T) * c           # exact dot products, then scaled
-            m_new = np.maximum(m, np.max(s, axis=1))
-            alpha = np.exp(m - m_new)                  # 0 for the first block (m = -inf)
-            L = L * alpha
-            acc = acc * alpha[:, None]
-            p = e4m3_decode(e4m3_encode(np.exp(s - m_new[:, None]) * E4M3_MAX))
-            L = L + np.sum(p, axis=1)
-            acc = acc + p @ v[j0:j1]
-            if return_weights:
-                w[:, :j0] *= alpha[:, None]
-                w[:, j0:j1] = p
-            m = m_new
-        out[r0:r1] = acc * float(scale_v) / L[:, None]
-        if return_weights:
-            weights[r0:r1] = w / L[:, None]
-            L_all[r0:r1] = L
-    if return_weights:
-        return out, weights, L_all
     return out
 
 
@@ -176,11 +117,11 @@ def _gather(groups, tokens, T):
 
 
 def fp8_attention(q8, k8, v8, cu_seqlens, scale_q, scale_k, scale_v, sm_scale,
-                  tokens=None, kv_block=None):
+                  tokens=None):
     """Packed varlen FP8 attention. q8/k8/v8: E4M3 codes [T, H, d].
 
     Returns O [len(tokens), H, d] (or [T, H, d] when tokens is None) in float64, each
-    sequence attending only to its own keys; kv_block as in fp8_attention_head.
+    sequence attending only to its own keys.
     """
     q8 = np.asarray(q8)
     T, H, d = q8.shape
@@ -193,8 +134,7 @@ def fp8_attention(q8, k8, v8, cu_seqlens, scale_q, scale_k, scale_v, sm_scale,
         dst = rows if pos is None else np.array([pos[int(r)] for r in rows])
         for h in range(H):
             out[dst, h] = fp8_attention_head(q8[rows, h], k8[lo:hi, h], v8[lo:hi, h],
-                                             scale_q, scale_k, scale_v, sm_scale,
-                                             kv_block=kv_block)
+                                             scale_q, scale_k, scale_v, sm_scale)
     return out
 
 

@@ -18,9 +18,15 @@ import oracle  # noqa: E402
 
 MAX_ABS_TOL = 1.5e-2     # attention output vs the oracle, unit-variance inputs
 MEAN_ABS_TOL = 2e-3
-# P is quantised relative to the running maximum over blocks of this many keys
-# (FP8ATTN_KV_BLOCK in include/fp8attn.h); the oracle follows the same rule.
-KV_BLOCK = 64
+# At most this fraction of the compared elements may exceed MAX_ABS_TOL, and each of those
+# only within its hardware bound (hw_bound_rows): the matrix core's accumulation error can
+# move a single E4M3 weight across a rounding midpoint, which on a short row moves the
+# output by more than the stated tolerance; the cap keeps the bound from absorbing any
+# number of such elements.
+OVER_TOL_CAP = 1e-3
+# keys per FP8 MFMA of the PV and row-sum products (the K dimension of one instruction):
+# the hardware bound groups their accumulation error by these blocks
+MFMA_KEYS = 64
 
 
 def bits(t: torch.Tensor) -> np.ndarray:
@@ -64,11 +70,10 @@ def sample_tokens(cu, per_seq_edge=64, per_seq_random=128, seed=0):
     return np.array(sorted(set(toks)), dtype=np.int64)
 
 
-def oracle_fp8_rows(q, k, v, cu, scales_qkv, sm_scale, tokens=None, kv_block=KV_BLOCK):
+def oracle_fp8_rows(q, k, v, cu, scales_qkv, sm_scale, tokens=None):
     """Oracle FP8 attention on the given bf16 tensors (GPU or CPU) for `tokens` rows.
 
-    scales_qkv: [(scale, inv)] * 3 as computed by the oracle. kv_block=None selects the
-    global-row-maximum reading instead of the online-softmax rule.
+    scales_qkv: [(scale, inv)] * 3 as computed by the oracle.
     """
     luts = [quant_lut(s[1]) for s in scales_qkv]
     qb, kb, vb = bits(q), bits(k), bits(v)
@@ -77,12 +82,12 @@ def oracle_fp8_rows(q, k, v, cu, scales_qkv, sm_scale, tokens=None, kv_block=KV_
     v8 = luts[2][vb]
     if tokens is None:
         return oracle.fp8_attention(q8, k8, v8, cu, scales_qkv[0][0], scales_qkv[1][0],
-                                    scales_qkv[2][0], sm_scale, kv_block=kv_block)
+                                    scales_qkv[2][0], sm_scale)
     # only the requested query rows need quantising
     q8 = np.zeros(qb.shape, dtype=np.uint8)
     q8[tokens] = luts[0][qb[tokens]]
     return oracle.fp8_attention(q8, k8, v8, cu, scales_qkv[0][0], scales_qkv[1][0],
-                                scales_qkv[2][0], sm_scale, tokens=tokens, kv_block=kv_block)
+                                scales_qkv[2][0], sm_scale, tokens=tokens)
 
 
 def oracle_ref_rows(q, k, v, cu, sm_scale, tokens=None):
@@ -141,18 +146,26 @@ def _max_products(q, k):
     return out.astype(np.float64)
 
 
-def hw_bound_rows(q8, k8, v8, cu, scales_qkv, sm_scale, tokens, kv_block=KV_BLOCK):
+def score_slack(s, m):
+    """Bound on the fp32 evaluation error of exp(s - m) * 448 in the kernel, in natural-log
+    units: the softmax constant c = scale_q * scale_k * sigma * log2 e and m * c -
+    log2 448 are each a few binary32 roundings, the exponent s * c - (m * c - log2 448) is
+    one FMA, and v_exp_f32 is within 1 ulp; 2^-21 (16 + |m| + |s - m|) covers them all."""
+    return 2.0 ** -21 * (16.0 + np.abs(m) + np.abs(s - m))
+
+
+def hw_bound_rows(q8, k8, v8, cu, scales_qkv, sm_scale, tokens):
     """Per (row, head, channel) bound on |O_gpu - O_oracle| from the FP8 MFMA error.
 
     q8/k8/v8: E4M3 codes [T, H, d] (q8 needs only the requested rows). For row r the score
     of key j may be off by e_j = c * 2 * 2^-11 * max_c |q_c k_jc| (two 64-channel
-    instructions); the running maximum by E = the largest e over the keys that hold a
-    block maximum. As in the online rule, the weight of key j in block b is quantised
-    relative to the running maximum m_b after that block, P~_j = exp(s_j - m_b) * 448, and
-    enters the output scaled by exp(m_b - m_final). Each quantised weight then lies between
-    the E4M3 codes of P~_j * exp(-+(e_j + 2E)), and the rescale factors within exp(+-2E);
-    the PV and row-sum products add 2^-11 of their largest product per 64-key instruction;
-    output rounding to bf16 adds 2^-9 |O|.
+    instructions) plus score_slack; the row maximum the kernel takes over those scores, by
+    E = max(e_j* at the argmax j*, max_j (s_j + e_j) - m). Each quantised weight
+    P~_j = exp(s_j - m) * 448 then lies between the E4M3 codes of P~_j * exp(-+(e_j + E)),
+    which moves O by at most sum_j width_j (|v_j| + |O|) / L_lo (L_lo: the row sum of the
+    lower codes); the PV and row-sum MFMAs add 2^-11 of their largest product per 64-key
+    instruction, fp32 accumulation over the key blocks 2^-24 per block, and the output's
+    rounding to bf16 2^-8 of its value.
     """
     sq, sk, sv = scales_qkv[0][0], scales_qkv[1][0], scales_qkv[2][0]
     c = sq * sk * sm_scale
@@ -163,60 +176,72 @@ def hw_bound_rows(q8, k8, v8, cu, scales_qkv, sm_scale, tokens, kv_block=KV_BLOC
         rows = lo + local
         dst = np.array([pos[int(r)] for r in rows])
         S = hi - lo
-        nblk = (S + kv_block - 1) // kv_block
+        nblk = (S + MFMA_KEYS - 1) // MFMA_KEYS
+        ar = np.arange(len(rows))
         for h in range(H):
             q = oracle.e4m3_decode(q8[rows, h])
             k = oracle.e4m3_decode(k8[lo:hi, h])
             v = oracle.e4m3_decode(v8[lo:hi, h]) * sv
             s = (q @ k.T) * c                                   # exact scores
-            e = c * 2 * MFMA_REL_ERR * _max_products(q, k)
-            E = np.zeros((len(rows), 1))
-            for bb in range(nblk):
-                j0, j1 = bb * kv_block, min(S, (bb + 1) * kv_block)
-                am = np.argmax(s[:, j0:j1], axis=1) + j0
-                E = np.maximum(E, e[np.arange(len(rows)), am][:, None])
-            m_final = s.max(axis=1, keepdims=True)
-            pt = np.zeros_like(s)                               # P~ against the running max
-            w = np.zeros_like(s)                                # its factor exp(m_b - m_final)
-            m_b = np.full((len(rows), 1), -np.inf)
-            for bb in range(nblk):
-                j0, j1 = bb * kv_block, min(S, (bb + 1) * kv_block)
-                m_b = np.maximum(m_b, s[:, j0:j1].max(axis=1, keepdims=True))
-                pt[:, j0:j1] = np.exp(s[:, j0:j1] - m_b) * oracle.E4M3_MAX
-                w[:, j0:j1] = np.exp(m_b - m_final)
-            lo8 = oracle.e4m3_decode(encode_nonneg(pt * np.exp(-(e + 2 * E)))) * w
-            hi8 = oracle.e4m3_decode(encode_nonneg(pt * np.exp(e + 2 * E))) * w
-            p = oracle.e4m3_decode(encode_nonneg(pt)) * w
+            m = s.max(axis=1, keepdims=True)
+            e = c * 2 * MFMA_REL_ERR * _max_products(q, k) + score_slack(s, m)
+            jstar = np.argmax(s, axis=1)
+            E = np.maximum(e[ar, jstar], (s + e).max(axis=1) - m[:, 0])[:, None]
+            pt = np.exp(s - m) * oracle.E4M3_MAX
+            lo8 = oracle.e4m3_decode(encode_nonneg(pt * np.exp(-(e + E))))
+            hi8 = oracle.e4m3_decode(encode_nonneg(pt * np.exp(e + E)))
+            p = oracle.e4m3_decode(encode_nonneg(pt))
             L = p.sum(axis=1, keepdims=True)
+            L_lo = lo8.sum(axis=1, keepdims=True)
             O = (p @ v) / L
-            dw = (hi8 - lo8) + p * (np.exp(2 * E) - 1.0)
-            b = (dw @ np.abs(v) + dw.sum(axis=1, keepdims=True) * np.abs(O)) / L
+            dw = hi8 - lo8
+            b = (dw @ np.abs(v) + dw.sum(axis=1, keepdims=True) * np.abs(O)) / L_lo
             pv = np.zeros_like(O)
             ls = np.zeros((len(rows), 1))
             for bb in range(nblk):
-                j0, j1 = bb * kv_block, min(S, (bb + 1) * kv_block)
-                pv += (p[:, j0:j1, None] * np.abs(v[None, j0:j1, :])).max(axis=1)
-                ls += p[:, j0:j1].max(axis=1, keepdims=True)
-            b += MFMA_REL_ERR * (pv + ls * np.abs(O)) / L
-            b += 2.0 ** -9 * np.abs(O)                           # bf16 output rounding
+                j0, j1 = bb * MFMA_KEYS, min(S, (bb + 1) * MFMA_KEYS)
+                pv += (hi8[:, j0:j1, None] * np.abs(v[None, j0:j1, :])).max(axis=1)
+                ls += hi8[:, j0:j1].max(axis=1, keepdims=True)
+            b += MFMA_REL_ERR * (pv + ls * np.abs(O)) / L_lo
+            b += nblk * 2.0 ** -24 * ((hi8 @ np.abs(v)) / L_lo + np.abs(O))
+            # the output is rounded to bf16 once (8 significant bits: at most 2^-8 of the
+            # value it rounds, which is within b of O)
+            b += 2.0 ** -8 * (np.abs(O) + b) * (1 + 2.0 ** -20)
             out[dst, h] = b
     return out
 
 
-def check_rows(got, want, bound, vstd, max_tol=MAX_ABS_TOL, mean_tol=MEAN_ABS_TOL):
-    """Parity verdict in unit-variance units (errors divided by the V channel std).
+def check_rows(got, want, vstd, bound_fn=None, max_tol=MAX_ABS_TOL, mean_tol=MEAN_ABS_TOL,
+               cap=OVER_TOL_CAP):
+    """Parity verdict in unit-variance units (errors divided by vstd, the V channel std:
+    1.0 for unit-variance inputs). got/want: [rows, H, d].
 
-    Every element must be within the stated max tolerance or within the hardware bound;
-    the mean must meet the stated mean tolerance. Returns a dict of statistics.
+    Every element must be within the stated max tolerance, except at most a fraction `cap`
+    of them, each within its hardware bound; the mean must meet the stated mean tolerance.
+    bound_fn(sel) returns hw_bound_rows for the rows `sel` (indices into got's first axis);
+    it is evaluated only for rows that hold an element over the stated tolerance. Without
+    it no element may exceed the tolerance. Returns a dict of statistics.
     """
     err = np.abs(got - want) / vstd
-    lim = np.maximum(max_tol, bound / vstd)
-    bad = err > lim
+    over = err > max_tol
+    n = int(err.size)
+    sel = np.nonzero(over.reshape(over.shape[0], -1).any(axis=1))[0]
+    n_over = int(over.sum())
+    if sel.size == 0:
+        n_bad, worst_ratio = 0, 0.0
+    elif bound_fn is None:
+        n_bad, worst_ratio = n_over, float("inf")
+    else:
+        lim = bound_fn(sel) / vstd
+        e_sel = err[sel]
+        bad = over[sel] & (e_sel > lim)
+        n_bad = int(bad.sum())
+        worst_ratio = float((e_sel[over[sel]] / lim[over[sel]]).max())
     stats = {"max_abs_norm": float(err.max()), "mean_abs_norm": float(err.mean()),
              "max_abs": float(np.abs(got - want).max()),
-             "n_over_stated": int((err > max_tol).sum()), "n_bad": int(bad.sum()),
-             "n": int(err.size)}
-    stats["ok"] = stats["n_bad"] == 0 and stats["mean_abs_norm"] <= mean_tol
+             "n_over_stated": n_over, "frac_over_stated": n_over / max(n, 1),
+             "n_over_bound": n_bad, "worst_over_stated_err_per_bound": worst_ratio, "n": n}
+    stats["ok"] = (n_bad == 0 and stats["mean_abs_norm"] <= mean_tol and n_over <= cap * n)
     return stats
 
 

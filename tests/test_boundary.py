@@ -185,14 +185,6 @@ def test_pad_start_regions_hold_their_sequences():
             assert starts[i + 1] - starts[i] >= (int(s) + 127) // 128 * 128
 
 
-def test_kv_block_constant_agrees():
-    import sys
-    sys.path.insert(0, os.path.dirname(__file__))
-    from parity_util import KV_BLOCK as ORACLE_BLOCK
-    m = re.search(r"#define FP8ATTN_KV_BLOCK (\d+)", open(HEADER).read())
-    assert int(m.group(1)) == fa.KV_BLOCK == ORACLE_BLOCK == 64
-
-
 def test_binding_rejects_host_tensors_before_any_gpu_call():
     # the Python binding refuses host memory (and non-tensors) for every device argument,
     # before the library sees an address

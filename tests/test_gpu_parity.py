@@ -203,10 +203,7 @@ def test_quantize_saturates_static():
     out = fa.attend(st, ws, _cu_dev(cu), cu, 2)
     torch.cuda.synchronize()
     got, want = bf16_to_f64(out), oracle_fp8_rows(q, k, v, cu, sc, SM)
-    luts = [quant_lut(x[1]) for x in sc]
-    bound = hw_bound_rows(luts[0][bits(q)], luts[1][bits(k)], luts[2][bits(v)], cu, sc, SM,
-                          np.arange(q.shape[0]))
-    stats = check_rows(got, want, bound, v_channel_std(v)[None])
+    stats = check_rows(got, want, v_channel_std(v)[None], _bound_fn(q, k, v, cu, sc, SM))
     say(f"  attention on saturated codes: {stats}")
     assert stats["ok"], stats
 
@@ -237,6 +234,14 @@ def _run_fp8(q, k, v, cu, static=None, margin=1.5, softmax_scale=0.0):
     return out, layer
 
 
+def _bound_fn(q, k, v, cu, sc, sm):
+    """hw_bound_rows for a subset of all rows (check_rows asks only for rows that hold an
+    element over the stated tolerance)."""
+    luts = [quant_lut(x[1]) for x in sc]
+    q8, k8, v8 = luts[0][bits(q)], luts[1][bits(k)], luts[2][bits(v)]
+    return lambda sel: hw_bound_rows(q8, k8, v8, cu, sc, sm, np.asarray(sel))
+
+
 def _assert_close(tag, got, want, max_tol=MAX_ABS_TOL, mean_tol=MEAN_ABS_TOL):
     mx, mn = compare(got, want)
     say(f"  {tag}: max-abs {mx:.3e} mean-abs {mn:.3e}")
@@ -254,19 +259,12 @@ def test_fp8_attention_all_rows(lens, H, outliers):
     sc = [oracle.scale_pair(a) for a in _amax3(q, k, v)]
     want = oracle_fp8_rows(q, k, v, cu, sc, SM)
     got = bf16_to_f64(out)
-    if not outliers:
-        # unit-variance inputs: the stated tolerance, nothing else
-        _assert_close("fp8 vs oracle (online rule)", got, want)
-    else:
-        # per-channel scaled inputs: unit-variance units, plus the FP8 matrix-core bound
-        luts = [quant_lut(x[1]) for x in sc]
-        toks = np.arange(q.shape[0])
-        bound = hw_bound_rows(luts[0][bits(q)], luts[1][bits(k)], luts[2][bits(v)], cu, sc, SM, toks)
-        st = check_rows(got, want, bound, v_channel_std(v)[None])
-        say(f"  fp8 vs oracle (unit-variance units): {st}")
-        assert st["ok"], st
-    mx_g, mn_g = compare(got, oracle_fp8_rows(q, k, v, cu, sc, SM, kv_block=None))
-    say(f"  (global-max reading: max-abs {mx_g:.3e} mean-abs {mn_g:.3e})")
+    # the stated tolerance (in unit-variance units where channels carry outliers), except a
+    # capped fraction of elements, each within the FP8 matrix core's per-element bound
+    st = check_rows(got, want, v_channel_std(v)[None] if outliers else 1.0,
+                    _bound_fn(q, k, v, cu, sc, SM))
+    say(f"  fp8 vs oracle: {st}")
+    assert st["ok"], st
     ref = oracle_ref_rows(q, k, v, cu, SM)
     c_gpu, c_or = cosine(got, ref), cosine(want, ref)
     say(f"  cosine vs unquantised: gpu {c_gpu:.6f} oracle {c_or:.6f}")
@@ -276,19 +274,16 @@ def test_fp8_attention_all_rows(lens, H, outliers):
 def test_fp8_attention_many_short_sequences():
     # unit-variance inputs, but rows of at most 199 keys: one E4M3 weight moved across a
     # rounding midpoint by the matrix core's accumulation error shifts a short row's output
-    # by up to a few 1e-2, so elements are held to the stated tolerance or to the
-    # per-element hardware bound, as for the inputs with outliers
+    # by up to a few 1e-2, so a capped fraction of elements may exceed the stated tolerance
+    # within the per-element hardware bound
     lens, H = _many_lens(6, 120, 200), 16
     say(f"fp8 attention {len(lens)} short sequences, H={H}")
     q, k, v, cu = random_varlen(lens, H, seed=78, device=DEV)
     out, _ = _run_fp8(q, k, v, cu)
     sc = [oracle.scale_pair(a) for a in _amax3(q, k, v)]
     got, want = bf16_to_f64(out), oracle_fp8_rows(q, k, v, cu, sc, SM)
-    luts = [quant_lut(x[1]) for x in sc]
-    toks = np.arange(q.shape[0])
-    bound = hw_bound_rows(luts[0][bits(q)], luts[1][bits(k)], luts[2][bits(v)], cu, sc, SM, toks)
-    st = check_rows(got, want, bound, v_channel_std(v)[None])
-    say(f"  fp8 vs oracle (unit-variance units): {st}")
+    st = check_rows(got, want, 1.0, _bound_fn(q, k, v, cu, sc, SM))
+    say(f"  fp8 vs oracle: {st}")
     assert st["ok"], st
 
 
@@ -322,11 +317,7 @@ def test_explicit_softmax_scale(sm):
     got, want = bf16_to_f64(out), oracle_fp8_rows(q, k, v, cu, sc, sm32)
     # the score error of the FP8 matrix core grows with the scale, so elements are held to
     # the stated tolerance or to the per-element hardware bound
-    luts = [quant_lut(x[1]) for x in sc]
-    toks = np.arange(q.shape[0])
-    bound = hw_bound_rows(luts[0][bits(q)], luts[1][bits(k)], luts[2][bits(v)], cu, sc, sm32,
-                          toks)
-    st = check_rows(got, want, bound, v_channel_std(v)[None])
+    st = check_rows(got, want, 1.0, _bound_fn(q, k, v, cu, sc, sm32))
     say(f"  fp8 vs oracle: {st}")
     assert st["ok"], st
     bout = fa.forward(None, q, k, v, _cu_dev(cu), cu, softmax_scale=sm, skip=True)

@@ -1,11 +1,12 @@
 """GPU parity on the five full-size workloads (shapes, seeds and value distributions of
 workloads.WORKLOADS), in the launch configuration the benchmark times.
 
-Bytes (amax, ring, scales, every E4M3 byte of Q8/K8/V8t) are compared bit-exactly where
-the oracle can stream them; attention is compared on sampled rows (first/last rows of
+Bytes (amax, ring, scales, every E4M3 byte of Q8/K8/V8t) are compared bit-exactly on every
+workload (for the 20-forward ring and the DiT schedule: at the checked forwards); attention is compared on sampled rows (first/last rows of
 every sequence plus seeded random rows, each row exact over all of its keys), in
 unit-variance units (error / std of the V channel) against the stated tolerance, with the
-per-element FP8 matrix-core bound of parity_util.hw_bound_rows on inputs with outliers.
+per-element FP8 matrix-core bound of parity_util.hw_bound_rows for a capped fraction of
+elements.
 """
 import numpy as np
 import pytest
@@ -68,18 +69,16 @@ def _check_bytes(ws, q, k, v, cu, sc):
             assert np.array_equal(got, want), ("v", i, h)
 
 
-def _fp8_parity(tag, out, q, k, v, cu, sc, toks, hw_bound):
+def _fp8_parity(tag, out, q, k, v, cu, sc, toks, unit_variance=False):
     got = bf16_to_f64(out[torch.as_tensor(toks, device=DEV)])
     want = oracle_fp8_rows(q, k, v, cu, sc, SM, tokens=toks)
-    vstd = v_channel_std(v)[None]
-    if hw_bound:
-        luts = [quant_lut(x[1]) for x in sc]
-        q8 = np.zeros(q.shape, np.uint8)
-        q8[toks] = luts[0][bits(q[torch.as_tensor(toks, device=DEV)])]
-        bound = hw_bound_rows(q8, luts[1][bits(k)], luts[2][bits(v)], cu, sc, SM, toks)
-    else:
-        bound = np.zeros_like(got)
-    st = check_rows(got, want, bound, vstd)
+    vstd = 1.0 if unit_variance else v_channel_std(v)[None]
+    luts = [quant_lut(x[1]) for x in sc]
+    q8 = np.zeros(q.shape, np.uint8)
+    q8[toks] = luts[0][bits(q[torch.as_tensor(toks, device=DEV)])]
+    k8, v8 = luts[1][bits(k)], luts[2][bits(v)]
+    st = check_rows(got, want, vstd,
+                    lambda sel: hw_bound_rows(q8, k8, v8, cu, sc, SM, toks[np.asarray(sel)]))
     ref = oracle_ref_rows(q, k, v, cu, SM, tokens=toks)
     st["cos_gpu_vs_unquantised"] = cosine(got, ref)
     st["cos_oracle_vs_unquantised"] = cosine(want, ref)
@@ -92,7 +91,7 @@ def _fp8_parity(tag, out, q, k, v, cu, sc, toks, hw_bound):
 def _bf16_parity(tag, out, q, k, v, cu, toks):
     got = bf16_to_f64(out[torch.as_tensor(toks, device=DEV)])
     want = oracle_ref_rows(q, k, v, cu, SM, tokens=toks)
-    st = check_rows(got, want, np.zeros_like(got), v_channel_std(v)[None])
+    st = check_rows(got, want, v_channel_std(v)[None])
     st["cos"] = cosine(got, want)
     say(f"  {tag}: {st}")
     assert st["ok"], st
@@ -115,7 +114,7 @@ def test_tiny_prefilled_ring_all_rows():
     sc = [oracle.scale_pair(a) for a in A]
     _check_bytes(layer._ws, q, k, v, cu, sc)
     toks = np.arange(w.total_tokens)
-    _fp8_parity("tiny fp8, all rows", out, q, k, v, cu, sc, toks, hw_bound=False)
+    _fp8_parity("tiny fp8, all rows", out, q, k, v, cu, sc, toks, unit_variance=True)
     skip = fa.forward(None, q, k, v, cu_d, cu, skip=True)
     _bf16_parity("tiny bf16, all rows", skip, q, k, v, cu, toks)
 
@@ -134,7 +133,7 @@ def test_kernel_point_sampled_rows():
     sc = [oracle.scale_pair(a) for a in A]
     _check_bytes(layer._ws, q, k, v, cu, sc)
     toks = sample_tokens(cu, 64, 128, seed=2)
-    _fp8_parity("kernel fp8, sampled rows", out, q, k, v, cu, sc, toks, hw_bound=True)
+    _fp8_parity("kernel fp8, sampled rows", out, q, k, v, cu, sc, toks)
     skip = fa.forward(None, q, k, v, cu_d, cu, skip=True)
     _bf16_parity("kernel bf16, sampled rows", skip, q, k, v, cu, toks)
 
@@ -155,17 +154,17 @@ def test_qhd_static_scales_sampled_rows():
     sc = [oracle.scale_pair(a) for a in A]
     _check_bytes(layer._ws, q, k, v, cu, sc)
     toks = sample_tokens(cu, 64, 128, seed=3)
-    _fp8_parity("qhd fp8 static, sampled rows", out, q, k, v, cu, sc, toks, hw_bound=True)
+    _fp8_parity("qhd fp8 static, sampled rows", out, q, k, v, cu, sc, toks)
 
 
-@pytest.mark.timeout(600)
+@pytest.mark.timeout(900)
 def test_4k_ring_over_20_forwards():
     w = WORKLOADS["4k"]
     say(f"workload {w.name}: {w.description}")
     cu, cu_d = _cu(w)
     layer = fa.AttentionLayer(DEV)
     ring = oracle.AmaxRing()
-    toks = sample_tokens(cu, 32, 64, seed=4)
+    toks = sample_tokens(cu, 64, 128, seed=4)
     for f in range(w.forwards):
         q, k, v = make_qkv(w, f, DEV)
         out = layer(q, k, v, cu_d, cu)
@@ -175,13 +174,16 @@ def test_4k_ring_over_20_forwards():
         if f in (16, w.forwards - 1):           # right after the first eviction, and the last
             say(f"  forward {f}: window max {A}")
             sc = [oracle.scale_pair(a) for a in A]
-            _fp8_parity(f"4k fp8 forward {f}, sampled rows", out, q, k, v, cu, sc, toks,
-                        hw_bound=True)
+            # every E4M3 byte of the one-pass dynamic quantisation (observe while quantising
+            # with the other 15 slots, then re-quantise where the window maximum moved)
+            _check_bytes(layer._ws, q, k, v, cu, sc)
+            say(f"  forward {f}: every byte of Q8, K8, V8t bit-exact")
+            _fp8_parity(f"4k fp8 forward {f}, sampled rows", out, q, k, v, cu, sc, toks)
         del q, k, v, out
     assert ring.count == 20
 
 
-@pytest.mark.timeout(900)
+@pytest.mark.timeout(1200)
 def test_dit_steps_layers_skip_routing():
     w = WORKLOADS["dit"]
     say(f"workload {w.name}: {w.description}")
@@ -189,7 +191,7 @@ def test_dit_steps_layers_skip_routing():
     steps, layers_sel = fa.parse_selector(w.skip_steps), fa.parse_selector(w.skip_layers)
     layers = [fa.AttentionLayer(DEV) for _ in range(w.layers)]
     rings = [oracle.AmaxRing() for _ in range(w.layers)]
-    toks = sample_tokens(cu, 16, 32, seed=5)
+    toks = sample_tokens(cu, 64, 128, seed=5)
     checked = set()
     for (f, step, layer, skip) in dit_schedule(w, steps, layers_sel):
         say(f"  forward {f}: step {step} layer {layer} {'bf16 (skip)' if skip else 'fp8'}")
@@ -208,7 +210,9 @@ def test_dit_steps_layers_skip_routing():
             _check_state(layers[layer].state, A, count=rings[layer].count, ring=rings[layer])
             if (step, layer) == (3, 7):
                 sc = [oracle.scale_pair(a) for a in A]
-                _fp8_parity("dit fp8 step 3 layer 7", out, q, k, v, cu, sc, toks, hw_bound=True)
+                _check_bytes(layers[layer]._ws, q, k, v, cu, sc)
+                say("  every byte of Q8, K8, V8t bit-exact")
+                _fp8_parity("dit fp8 step 3 layer 7", out, q, k, v, cu, sc, toks)
                 checked.add("fp8")
         del q, k, v, out
     counts = [int(fa.read_state(l.state)["count"]) for l in layers]

@@ -93,16 +93,15 @@ CASES = [
     ("amax of signed values", SCALING,
      [("return float(np.max(np.abs(x)))", "return float(np.max(x))")],
      [lambda: TS.test_amax_vs_integer_bits(0)]),
-    ("online rule: row sum not rescaled", ATT,
-     [("            L = L * alpha\n", "")],
-     [TA.test_online_weights_sum_to_one_and_constant_v, TA.test_online_two_key_closed_form]),
-    ("online rule: output not rescaled", ATT,
-     [("            acc = acc * alpha[:, None]\n", "")],
-     [TA.test_online_weights_sum_to_one_and_constant_v, TA.test_online_two_key_closed_form]),
-    ("online rule: softmax scale dropped", ATT,
-     [("s = (q[r0:r1] @ k[j0:j1].T) * c",
-       "s = (q[r0:r1] @ k[j0:j1].T) * float(scale_q) * float(scale_k)")],
-     [TA.test_online_two_key_closed_form, TA.test_online_equals_global_when_first_block_holds_max]),
+    ("row maximum over the first 64 keys only", ATT,
+     [("m = np.max(s, axis=1, keepdims=True)", "m = np.max(s[:, :64], axis=1, keepdims=True)")],
+     [TA.test_weights_sum_to_one_and_key_permutation, TA.test_row_maximum_over_all_keys_not_a_prefix]),
+    ("softmax scale dropped", ATT,
+     [("        s = raw * c\n", "        s = raw * float(scale_q) * float(scale_k)\n")],
+     [TA.test_worked_two_key_example]),
+    ("P scaled by 224 instead of 448", ATT,
+     [("p8 = e4m3_encode(p_tilde * E4M3_MAX)", "p8 = e4m3_encode(p_tilde * 224.0)")],
+     [TA.test_worked_two_key_example, TA.test_weights_sum_to_one_and_key_permutation]),
     ("normalised by the unquantised weights", ATT,
      [("        L = np.sum(p, axis=1)", "        L = np.sum(p_tilde * E4M3_MAX, axis=1)")],
      [TA.test_worked_two_key_example, TA.test_weights_sum_to_one_and_key_permutation]),
@@ -113,7 +112,7 @@ CASES = [
     ("a sequence sees the next sequence's first key", ATT,
      [("fp8_attention_head(q8[rows, h], k8[lo:hi, h], v8[lo:hi, h],",
        "fp8_attention_head(q8[rows, h], k8[lo:hi + 1, h], v8[lo:hi + 1, h],")],
-     [TA.test_block_diagonal_isolation_brute_force, TA.test_online_brute_force_varlen]),
+     [TA.test_block_diagonal_isolation_brute_force]),
     ("reference softmax normalised over the keys' axis", ATT,
      [("out[r0:r1] = (p @ v) / np.sum(p, axis=1, keepdims=True)",
        "out[r0:r1] = (p @ v) / np.sum(p, axis=0, keepdims=True)[:, :1]")],
