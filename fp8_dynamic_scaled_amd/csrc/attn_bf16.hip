@@ -130,17 +130,18 @@ __device__ __forceinline__ void pin(const uint4* p) {
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                       const uint16_t* __restrict__ v, const int32_t* __restrict__ cu,
-                      int num_seqs, int H, int qtiles, int units_per_xcd, float sm_scale,
+                      int num_seqs, int H, int vtiles, int units_per_xcd, float sm_scale,
                       uint16_t* __restrict__ out) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[4 * kTileBytes];
 
+  // ---- work unit: XCD-aware decode, virtual tile fastest (vtile_seq), then head
   const int L = blockIdx.x;
   const int unit = (L & 7) * units_per_xcd + (L >> 3);
-  const int qt = unit % qtiles;
-  const int sh = unit / qtiles;
-  const int head = sh % H;
-  const int seq = sh / H;
-  if (seq >= num_seqs) return;
+  const int vt = unit % vtiles;
+  const int head = unit / vtiles;
+  if (head >= H) return;
+  const int seq = vtile_seq(cu, num_seqs, vt);
+  const int qt = vt - vtile_start(cu, seq);
   const int seq_begin = cu[seq];
   const int S = cu[seq + 1] - seq_begin;
   if (qt * kBM >= S) return;
@@ -473,12 +474,13 @@ void attn_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
 hipError_t launch_attn_bf16(const AttnLaunch& a, const uint16_t* q, const uint16_t* k,
                             const uint16_t* v, hipStream_t s) {
   if (a.max_seqlen <= 0) return hipSuccess;
-  const int qtiles = (a.max_seqlen + kBM - 1) / kBM;
-  const int64_t units = (int64_t)a.num_seqs * a.H * qtiles;
+  static_assert(kBM == 128, "virtual tiles are 128 queries");
+  const int64_t vtiles = (a.T + 127) / 128 + a.num_seqs;   // per head, see vtile_start
+  const int64_t units = vtiles * a.H;
   const int64_t per_xcd = (units + 7) / 8;
   if (per_xcd * 8 > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL(attn_bf16_kernel, dim3((unsigned)(per_xcd * 8)), dim3(kThreads), 0, s, q,
-                     k, v, a.cu, a.num_seqs, a.H, qtiles, (int)per_xcd, a.softmax_scale,
+                     k, v, a.cu, a.num_seqs, a.H, (int)vtiles, (int)per_xcd, a.softmax_scale,
                      a.out);
   return hipGetLastError();
 }

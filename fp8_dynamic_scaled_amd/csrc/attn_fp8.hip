@@ -48,8 +48,10 @@
 //     iteration of each pass;
 //   * exp(s - m) * 448 is computed as exp2(s * c - (m * c - log2 448)), c = scales *
 //     log2(e): one FMA and one v_exp_f32 per score;
-//   * block -> work mapping is XCD-aware: consecutive work units (q-tiles of one
-//     (sequence, head)) go to the same XCD so its L2 keeps that head's K/V.
+//   * block -> work mapping is XCD-aware: consecutive work units (the q-tiles of one head,
+//     sequence after sequence) go to the same XCD so its L2 keeps that head's K/V; units
+//     are enumerated over virtual tiles (vtile_start), so a batch of very unequal
+//     sequences launches about one block per real q-tile.
 #include "device_common.h"
 #include "launch.h"
 
@@ -209,20 +211,20 @@ __device__ __forceinline__ void pin(const v8i& p) {
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__ k8,
                      const uint8_t* __restrict__ v8t, const int32_t* __restrict__ cu,
-                     int num_seqs, int H, int64_t Tp, int qtiles, int units_per_xcd,
+                     int num_seqs, int H, int64_t Tp, int vtiles, int units_per_xcd,
                      const fp8attn_state* __restrict__ st, float sm_scale,
                      uint16_t* __restrict__ out) {
   // kStages K tiles, then kStages V8t tiles
   __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * (kKTileBytes + kVTileBytes)];
 
-  // ---- work unit: XCD-aware decode, q-tile fastest
+  // ---- work unit: XCD-aware decode, virtual tile fastest (vtile_seq), then head
   const int L = blockIdx.x;
   const int unit = (L & 7) * units_per_xcd + (L >> 3);
-  const int qt = unit % qtiles;
-  const int sh = unit / qtiles;
-  const int head = sh % H;
-  const int seq = sh / H;
-  if (seq >= num_seqs) return;
+  const int vt = unit % vtiles;
+  const int head = unit / vtiles;
+  if (head >= H) return;
+  const int seq = vtile_seq(cu, num_seqs, vt);
+  const int qt = vt - vtile_start(cu, seq);
   const int seq_begin = cu[seq];
   const int S = cu[seq + 1] - seq_begin;
   if (qt * kBM >= S) return;
@@ -529,12 +531,13 @@ void attn_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__
 hipError_t launch_attn_fp8(const AttnLaunch& a, const fp8attn_state* st, const uint8_t* q8,
                            const uint8_t* k8, const uint8_t* v8t, hipStream_t s) {
   if (a.max_seqlen <= 0) return hipSuccess;
-  const int qtiles = (a.max_seqlen + kBM - 1) / kBM;
-  const int64_t units = (int64_t)a.num_seqs * a.H * qtiles;
+  static_assert(kBM == 128, "virtual tiles are 128 queries");
+  const int64_t vtiles = (a.T + 127) / 128 + a.num_seqs;   // per head, see vtile_start
+  const int64_t units = vtiles * a.H;
   const int64_t per_xcd = (units + 7) / 8;
   if (per_xcd * 8 > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL(attn_fp8_kernel, dim3((unsigned)(per_xcd * 8)), dim3(kThreads), 0, s, q8,
-                     k8, v8t, a.cu, a.num_seqs, a.H, a.Tp, qtiles, (int)per_xcd, st,
+                     k8, v8t, a.cu, a.num_seqs, a.H, a.Tp, (int)vtiles, (int)per_xcd, st,
                      a.softmax_scale, a.out);
   return hipGetLastError();
 }

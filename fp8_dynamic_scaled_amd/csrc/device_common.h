@@ -125,6 +125,30 @@ __device__ __forceinline__ bool wave_any(bool p) {
   return __builtin_amdgcn_ballot_w64(p) != 0;
 }
 
+// Work units of the attention kernels: the 128-query tiles of every (sequence, head). For
+// each head they are enumerated over "virtual tiles", the 128-column tiles of the padded
+// key range of V8t: sequence i owns virtual tiles [vtile_start(i), vtile_start(i+1)) with
+// vtile_start(i) = ceil(cu_i / 128) + i, its q-tiles are the first ceil(S_i / 128) of them
+// and the rest (at most two per sequence) are empty. A head has ceil(T / 128) + num_seqs
+// virtual tiles, so a batch of very unequal sequences launches about one block per real
+// q-tile, not num_seqs times the longest sequence's count.
+__device__ __forceinline__ int vtile_start(const int32_t* cu, int i) {
+  return ((cu[i] + 127) >> 7) + i;
+}
+// The sequence owning virtual tile vt: the largest i with vtile_start(i) <= vt (starts
+// strictly increase; vtile_start(0) = 0). A binary search on block-uniform loads.
+__device__ __forceinline__ int vtile_seq(const int32_t* cu, int num_seqs, int vt) {
+  int lo = 0, hi = num_seqs - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (vtile_start(cu, mid) <= vt)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  return lo;
+}
+
 // Start column of sequence i in the key-contiguous V8t layout (see fp8attn.h).
 __device__ __host__ __forceinline__ int64_t pad_start(int64_t cu_i, int i) {
   return ((cu_i + 127) / 128) * 128 + 128 * (int64_t)i;

@@ -18,12 +18,17 @@ import oracle  # noqa: E402
 
 MAX_ABS_TOL = 1.5e-2     # attention output vs the oracle, unit-variance inputs
 MEAN_ABS_TOL = 2e-3
-# At most this fraction of the compared elements may exceed MAX_ABS_TOL, and each of those
-# only within its hardware bound (hw_bound_rows): the matrix core's accumulation error can
-# move a single E4M3 weight across a rounding midpoint, which on a short row moves the
-# output by more than the stated tolerance; the cap keeps the bound from absorbing any
-# number of such elements.
-OVER_TOL_CAP = 1e-3
+# At most a fraction of the compared elements may exceed MAX_ABS_TOL, and each of those only
+# within its hardware bound (hw_bound_rows): the matrix core's accumulation error can move a
+# single E4M3 weight across a rounding midpoint, which on a short row moves the output by
+# more than the stated tolerance; the cap keeps the bound from absorbing any number of such
+# elements. The error is relative to the largest product of a score, so it, and the number
+# of moved weights, grow with outlier channels:
+#   unit-variance inputs (the regime the stated tolerance is for): 1e-4 (measured: at most
+#   2.1e-6, on rows of fewer than 200 keys);
+#   inputs with x20 outlier channels: 5e-3 (measured: at most 1.6e-3, rows of 77-300 keys).
+OVER_TOL_CAP = 1e-4
+OVER_TOL_CAP_OUTLIERS = 5e-3
 # keys per FP8 MFMA of the PV and row-sum products (the K dimension of one instruction):
 # the hardware bound groups their accumulation error by these blocks
 MFMA_KEYS = 64
