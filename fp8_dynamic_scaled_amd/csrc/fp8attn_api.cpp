@@ -225,6 +225,15 @@ int fp8attn_scales(void* state, int mode, const float* static_amax_host, float m
                     t, (double)static_amax_host[t]);
     if (!std::isfinite(margin) || !(margin > 0.0f))
       return fail(FP8ATTN_EINVAL, "fp8attn_scales: margin %g must be finite and > 0", (double)margin);
+    // the scales kernel forms A = fp32(amax * margin); an overflow to inf would give a zero
+    // inverse scale (every code 0) and NaN attention output
+    for (int t = 0; t < 3; ++t) {
+      volatile float a = static_amax_host[t] * margin;   // the binary32 product, as on the device
+      if (!std::isfinite(a))
+        return fail(FP8ATTN_EINVAL,
+                    "fp8attn_scales: static amax[%d] x margin = %g x %g overflows binary32", t,
+                    (double)static_amax_host[t], (double)margin);
+    }
   }
   return hip_status(fp8attn::launch_scales(static_cast<fp8attn_state*>(state), mode,
                                            mode == FP8ATTN_STATIC ? static_amax_host : nullptr,

@@ -139,7 +139,8 @@ int fp8attn_observe_amax(void* state, const void* q, const void* k, const void* 
  *     fp32(448/A'), each a correctly rounded division; cur is cleared.
  * One single-wave launch; no host synchronisation.
  * Errors: EINVAL for a NULL state, an unknown mode, a NULL static_amax_host in static
- * mode, a static amax that is negative or not finite, a margin that is not > 0 and finite.
+ * mode, a static amax that is negative or not finite, a margin that is not > 0 and finite,
+ * or a product fp32(static amax * margin) that overflows to infinity.
  */
 int fp8attn_scales(void* state, int mode, const float* static_amax_host, float margin,
                    void* stream);

@@ -122,6 +122,9 @@ def test_scales_and_observe_reject(lib):
     assert "mode" in lib.fp8attn_last_error().decode()
     assert lib.fp8attn_scales(P, 1, None, ctypes.c_float(1.5), NULL) == -1
     assert lib.fp8attn_scales(P, 1, f3(1.0, -2.0, 3.0), ctypes.c_float(1.5), NULL) == -1
+    # amax and margin each finite, their binary32 product not: rejected before any launch
+    assert lib.fp8attn_scales(P, 1, f3(1.0, 3.0e38, 3.0), ctypes.c_float(1.5), NULL) == -1
+    assert "overflows" in lib.fp8attn_last_error().decode()
     assert lib.fp8attn_scales(P, 1, f3(1.0, float("inf"), 3.0), ctypes.c_float(1.5), NULL) == -1
     assert lib.fp8attn_scales(P, 1, f3(1.0, 2.0, 3.0), ctypes.c_float(0.0), NULL) == -1
     assert lib.fp8attn_scales(P, 1, f3(1.0, 2.0, 3.0), ctypes.c_float(float("nan")), NULL) == -1

@@ -114,9 +114,16 @@ def test_static_scales_many_values_bit_exact():
             trio = [float(x) for x in vals[i:i + 3]]
             if len(trio) < 3:
                 break
+            A = oracle.static_amax(trio, margin)
+            if not all(math.isfinite(a) for a in A):
+                # amax x margin overflows binary32: rejected on the host, state untouched
+                before = st.clone()
+                with pytest.raises(_lib.Fp8AttnError, match="overflows"):
+                    fa.scales(st, "static", trio, margin)
+                assert torch.equal(st, before)
+                continue
             fa.scales(st, "static", trio, margin)
             s = fa.read_state(st)
-            A = oracle.static_amax(trio, margin)
             for t in range(3):
                 sc, inv = oracle.scale_pair(A[t])
                 assert float(s["amax"][t]) == A[t]
