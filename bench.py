@@ -70,6 +70,9 @@ def parse():
                     help="skip the quantisation measurements beyond the Infinity Cache")
     ap.add_argument("--no-regime", action="store_true",
                     help="skip the image-resolution sweep and the DiT-forward comparison")
+    ap.add_argument("--regime-case", default=None,
+                    help="run only the resolution case of this name (for profiling) and print "
+                         "its row")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the benchmark, run one plain device copy of this many MiB "
                          "(reference for HBM byte counters)")
@@ -345,7 +348,7 @@ def _median_burst_ms(fn, burst_ms=25.0, bursts=3):
     return t[len(t) // 2]
 
 
-def regime(fa, dev, settle_ms=60.0):
+def regime(fa, dev, settle_ms=60.0, only=None):
     """FP8 dynamic step (one-pass quantise + FP8 attention) against the BF16 kernel on
     3-image batches per resolution (16 heads, bf16 N(0,1) with x20 outlier columns), and on
     one forward of the DiT video workload (57600 tokens, 40 heads)."""
@@ -365,6 +368,10 @@ def regime(fa, dev, settle_ms=60.0):
     # one GPU's share of that forward under head (Ulysses) sharding of degree 4
     cases.append(("DiT forward, one of 4 head shards (H=10)",
                   Workload("dit-shard", 5, (0, 57600), 10, outliers=True)))
+    if only is not None:
+        cases = [c for c in cases if c[0] == only]
+        if not cases:
+            raise SystemExit(f"no resolution case named {only!r}")
     for name, w in cases:
         q, k, v = make_qkv(w, 0, dev)
         cu = np.asarray(w.cu_seqlens, dtype=np.int32)
@@ -444,6 +451,12 @@ def main():
     import torch
     import fp8_dynamic_scaled_amd as fa
     from workloads import WORKLOADS, make_qkv
+
+    if args.regime_case is not None:
+        dev = torch.device("cuda", 0)
+        torch.cuda.set_device(dev)
+        print(json.dumps({"resolution_case": regime(fa, dev, args.settle_ms, args.regime_case)}))
+        return
 
     w = WORKLOADS[args.workload]
     dev = torch.device("cuda", 0)
