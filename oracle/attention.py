@@ -12,13 +12,21 @@ The pages print no formula, so the attention is the textbook definition applied 
 packed sequence (block-diagonal, non-causal), with these readings:
   * softmax scale sigma is an explicit argument (1/sqrt(d) by default);
   * scores use the dequantised E4M3 operands: s_j = (q8 . k8_j) * scale_q * scale_k * sigma;
-  * P is quantised with the fixed scale 448 relative to the row maximum m = max_j s_j over
-    all keys of the row's sequence, so that P~_j = exp(s_j - m) lies in (0, 1] and
-    p8_j = E4M3(P~_j * 448);
+  * P is quantised with a scale of 448 times a power of two: with m = max_j s_j, the row
+    maximum over all keys of the row's sequence, and the reference exponent
+    M = ceil(m * log2 e), P~_j = 2^(s_j log2 e - M) lies in (0, 1] (the largest weight in
+    (1/2, 1]) and p8_j = E4M3(448 P~_j), so the largest code is in [224, 448];
   * the weights are the quantised p8_j normalised by their own sum (rows of weights sum
     to 1 and a constant V comes out unchanged); O is multiplied by scale_v.
-The maximum is the row's own, over every key: no page fixes a block of keys, so how an
-implementation tiles the keys is not part of the result.
+The pages fix no scale for P. The reference is the row's own maximum, over every key (no
+page fixes a block of keys, so how an implementation tiles them is not part of the
+result), rounded up to a power of two: E4M3 rounding commutes with multiplication by a
+power of two wherever both values are normal (>= 2^-6), so the weights of keys with
+s_j log2 e <= M', taken against an integer reference exponent M' <= M and later
+multiplied by 2^(M' - M), are these weights (away from that subnormal range). A flash-attention pass that finds the maximum as it
+visits the keys can therefore reach this result without a second pass over them; with
+the exact maximum as the reference it could not. Any reference in [m, m + ln 2) keeps
+the largest weight where E4M3 has its full 3-bit precision; this one is the power of two.
 Exactness: E4M3 values are multiples of 2^-9 below 2^9, so every product is a multiple
 of 2^-18 below 2^18; the d = 128 score sum stays below 2^43 units and the PV sum over
 up to ~2^17 keys below 2^53 units -- both are exact in float64 whatever the summation
@@ -27,12 +35,15 @@ Rows of a sequence are independent; they are evaluated in groups of rows only to
 memory, which changes no arithmetic.
 """
 
+import math
+
 import numpy as np
 
 from .e4m3 import E4M3_MAX, e4m3_decode, e4m3_encode
 from .numerics import bf16_bits_to_f64
 
 _ROW_GROUP = 512
+_LOG2E = 1.0 / math.log(2.0)
 
 
 def fp8_attention_head(q8, k8, v8, scale_q, scale_k, scale_v, sm_scale,
@@ -56,8 +67,9 @@ def fp8_attention_head(q8, k8, v8, scale_q, scale_k, scale_v, sm_scale,
         r1 = min(R, r0 + _ROW_GROUP)
         raw = q[r0:r1] @ k.T                      # exact
         s = raw * c
-        m = np.max(s, axis=1, keepdims=True)
-        p_tilde = np.exp(s - m)                   # in (0, 1]
+        t = s * _LOG2E                            # scores in log2 units
+        M = np.ceil(np.max(t, axis=1, keepdims=True))   # reference exponent of the row
+        p_tilde = np.exp2(t - M)                  # in (0, 1], the largest in (1/2, 1]
         p8 = e4m3_encode(p_tilde * E4M3_MAX)
         p = e4m3_decode(p8)
         L = np.sum(p, axis=1)                     # exact (multiples of 2^-9, < 2^53 units)

@@ -118,6 +118,7 @@ def cosine(a: np.ndarray, b: np.ndarray) -> float:
 # 2^-11.1 for a two-instruction d = 128 sum). The attention parity therefore allows, on
 # top of the stated tolerance, the output change those score/PV/row-sum errors can cause.
 MFMA_REL_ERR = 2.0 ** -11          # per instruction, relative to its largest |product|
+_LOG2E = 1.0 / math.log(2.0)
 
 
 _NONNEG_VALUES = oracle.e4m3_decode(np.arange(0x7F, dtype=np.uint8))   # codes 0x00..0x7E
@@ -152,10 +153,11 @@ def _max_products(q, k):
 
 
 def score_slack(s, m):
-    """Bound on the fp32 evaluation error of exp(s - m) * 448 in the kernel, in natural-log
-    units: the softmax constant c = scale_q * scale_k * sigma * log2 e and m * c -
-    log2 448 are each a few binary32 roundings, the exponent s * c - (m * c - log2 448) is
-    one FMA, and v_exp_f32 is within 1 ulp; 2^-21 (16 + |m| + |s - m|) covers them all."""
+    """Bound on the fp32 evaluation error of 448 * 2^(s log2 e - M) in the kernel, in
+    natural-log units: the softmax constant c = scale_q * scale_k * sigma * log2 e is a few
+    binary32 roundings, M - log2 448 one more, the exponent s * c - (M - log2 448) is one
+    FMA, and v_exp_f32 is within 1 ulp; with M < m log2 e + 1, 2^-21 (16 + |m| + |s - m|)
+    covers them all."""
     return 2.0 ** -21 * (16.0 + np.abs(m) + np.abs(s - m))
 
 
@@ -164,13 +166,18 @@ def hw_bound_rows(q8, k8, v8, cu, scales_qkv, sm_scale, tokens):
 
     q8/k8/v8: E4M3 codes [T, H, d] (q8 needs only the requested rows). For row r the score
     of key j may be off by e_j = c * 2 * 2^-11 * max_c |q_c k_jc| (two 64-channel
-    instructions) plus score_slack; the row maximum the kernel takes over those scores, by
-    E = max(e_j* at the argmax j*, max_j (s_j + e_j) - m). Each quantised weight
-    P~_j = exp(s_j - m) * 448 then lies between the E4M3 codes of P~_j * exp(-+(e_j + E)),
-    which moves O by at most sum_j width_j (|v_j| + |O|) / L_lo (L_lo: the row sum of the
-    lower codes); the PV and row-sum MFMAs add 2^-11 of their largest product per 64-key
-    instruction, fp32 accumulation over the key blocks 2^-24 per block, and the output's
-    rounding to bf16 2^-8 of its value.
+    instructions) plus score_slack. The kernel's reference exponent, taken from its own
+    scores (and, before the last key tile, from the running maximum), differs from the
+    oracle's M only by whole powers of two, which scale every weight and the row sum alike
+    and so leave O unchanged -- except where a weight falls below E4M3's normal range
+    (2^-6) on one of the grids, where the two roundings differ by at most 2^-9 at the
+    oracle's scale (the kernel's grid is at most twice as coarse, 2^-8 apart). So each
+    weight lies between the E4M3 codes of 448 * 2^(s_j log2 e - M) * exp(-+e_j), widened by
+    2^-9 on each side when the upper value is below 2^-5; that moves O by at most
+    sum_j width_j (|v_j| + |O|) / L_lo (L_lo: the row sum of the lower ends); the PV and
+    row-sum MFMAs add 2^-11 of their largest product per 64-key instruction, fp32
+    accumulation over the key blocks 2^-24 per block (the power-of-two rescales of the
+    partial sums are exact), and the output's rounding to bf16 2^-8 of its value.
     """
     sq, sk, sv = scales_qkv[0][0], scales_qkv[1][0], scales_qkv[2][0]
     c = sq * sk * sm_scale
@@ -182,7 +189,6 @@ def hw_bound_rows(q8, k8, v8, cu, scales_qkv, sm_scale, tokens):
         dst = np.array([pos[int(r)] for r in rows])
         S = hi - lo
         nblk = (S + MFMA_KEYS - 1) // MFMA_KEYS
-        ar = np.arange(len(rows))
         for h in range(H):
             q = oracle.e4m3_decode(q8[rows, h])
             k = oracle.e4m3_decode(k8[lo:hi, h])
@@ -190,11 +196,12 @@ def hw_bound_rows(q8, k8, v8, cu, scales_qkv, sm_scale, tokens):
             s = (q @ k.T) * c                                   # exact scores
             m = s.max(axis=1, keepdims=True)
             e = c * 2 * MFMA_REL_ERR * _max_products(q, k) + score_slack(s, m)
-            jstar = np.argmax(s, axis=1)
-            E = np.maximum(e[ar, jstar], (s + e).max(axis=1) - m[:, 0])[:, None]
-            pt = np.exp(s - m) * oracle.E4M3_MAX
-            lo8 = oracle.e4m3_decode(encode_nonneg(pt * np.exp(-(e + E))))
-            hi8 = oracle.e4m3_decode(encode_nonneg(pt * np.exp(e + E)))
+            t = s * _LOG2E
+            M = np.ceil(t.max(axis=1, keepdims=True))
+            pt = np.exp2(t - M) * oracle.E4M3_MAX
+            sub = np.where(pt * np.exp(e) < 2.0 ** -5, 2.0 ** -9, 0.0)
+            lo8 = np.maximum(oracle.e4m3_decode(encode_nonneg(pt * np.exp(-e))) - sub, 0.0)
+            hi8 = oracle.e4m3_decode(encode_nonneg(pt * np.exp(e))) + sub
             p = oracle.e4m3_decode(encode_nonneg(pt))
             L = p.sum(axis=1, keepdims=True)
             L_lo = lo8.sum(axis=1, keepdims=True)

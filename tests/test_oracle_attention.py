@@ -2,10 +2,16 @@
 
 * Q = 0 gives uniform weights, so O is the textbook mean of dec(v8) * scale_v;
 * a single key gives O = dec(v8) * scale_v; a constant V comes out unchanged;
-* a worked two-key case whose scores differ by ln 3: the max key gets p8 = 448 and the
-  other E4M3(448/3) = 144, so O = (448 v1 + 144 v2) / 592 (normalising by the quantised
-  weights; dividing by the unquantised sum would give 597.33 instead);
-* weight rows sum to 1; permuting keys (with their values) changes nothing;
+* a worked two-key case with scores of 2.5 and 1.25 in log2 units: the reference
+  exponent is 3, the weights E4M3(448 * 2^-0.5 = 316.8) = 320 and E4M3(448 * 2^-1.75 =
+  133.2) = 128, so O = (320 v1 + 128 v2) / 448 (normalising by the quantised weights;
+  dividing by the unquantised sum would give 450.0 instead; the exact maximum as the
+  reference would give weights 448 and 192);
+* weight rows sum to 1, the largest weight of a row is in [224, 448]; permuting keys
+  (with their values) changes nothing;
+* a single pass over 64-key blocks that takes each block's weights against the running
+  reference exponent and rescales the partial sums by powers of two gives the same
+  result (the property that lets a kernel find the maximum as it goes);
 * packed varlen results equal separate per-sequence calls, which equal a dense
   block-diagonal-masked brute force written with pure-Python loops (T <= 64, H = 2);
 * the float64 reference attention equals scipy's softmax-based formula (a library
@@ -62,8 +68,9 @@ def test_single_key_and_constant_v():
 
 
 def test_worked_two_key_example():
-    # q . k1 = 8, q . k2 = 4 (raw dot products of E4M3 values); sigma chosen so the
-    # score gap is ln 3: P~ = (1, 1/3), p8 = (448, E4M3(149.33) = 144).
+    # q . k1 = 8, q . k2 = 4 (raw dot products of E4M3 values); sigma = 0.3125 ln 2 puts
+    # the scores at 2.5 and 1.25 in log2 units: M = 3, P~ = (2^-0.5, 2^-1.75),
+    # p8 = (E4M3(316.78) = 320, E4M3(133.19) = 128).
     q8 = np.zeros((1, D), np.uint8)
     k8 = np.zeros((2, D), np.uint8)
     q8[0, 0] = e4m3_encode(np.array([2.0]))[0]
@@ -72,12 +79,12 @@ def test_worked_two_key_example():
     v8 = np.zeros((2, D), np.uint8)
     v8[0, :] = e4m3_encode(np.array([1.0]))[0]
     v8[1, :] = e4m3_encode(np.array([-2.0]))[0]
-    sigma = math.log(3.0) / 4.0
+    sigma = 0.3125 * math.log(2.0)
     out, p8, L = oracle.fp8_attention_head(q8, k8, v8, 1.0, 1.0, 1.0, sigma,
                                            return_weights=True)
-    assert list(e4m3_decode(p8[0])) == [448.0, 144.0]
-    assert L[0] == 592.0
-    assert np.allclose(out[0], (448.0 * 1.0 + 144.0 * -2.0) / 592.0, rtol=1e-15)
+    assert list(e4m3_decode(p8[0])) == [320.0, 128.0]
+    assert L[0] == 448.0
+    assert np.allclose(out[0], (320.0 * 1.0 + 128.0 * -2.0) / 448.0, rtol=1e-15)
 
 
 def test_weights_sum_to_one_and_key_permutation():
@@ -90,7 +97,9 @@ def test_weights_sum_to_one_and_key_permutation():
                                            return_weights=True)
     w = e4m3_decode(p8) / L[:, None]
     assert np.allclose(w.sum(axis=1), 1.0, rtol=0, atol=1e-14)
-    assert np.all(e4m3_decode(p8).max(axis=1) == 448.0)   # the row maximum maps to 448
+    top = e4m3_decode(p8).max(axis=1)           # the row maximum maps to 448 * (1/2, 1]
+    assert np.all((top >= 224.0) & (top <= 448.0))
+    assert len(set(top)) > 1                    # and not to one fixed code
     perm = rng.permutation(S)
     out2 = oracle.fp8_attention_head(q8, k8[perm], v8[perm], 0.02, 0.03, 0.004,
                                      1 / math.sqrt(D))
@@ -117,13 +126,14 @@ def _brute_force_dense(q8, k8, v8, cu, sq, sk, sv, sigma):
                 for c in range(d):
                     acc += dq[r, h, c] * dk[j, h, c]
                 scores.append(acc * sq * sk * sigma)
-            m = max(scores)
+            M = math.ceil(max(scores) / math.log(2.0))
             p = []
             for s in scores:
                 if s == -math.inf:
                     p.append(0.0)
                 else:
-                    p.append(float(e4m3_decode(e4m3_encode(np.array([math.exp(s - m) * 448.0])))[0]))
+                    x = 448.0 * 2.0 ** (s / math.log(2.0) - M)
+                    p.append(float(e4m3_decode(e4m3_encode(np.array([x])))[0]))
             L = sum(p)
             for c in range(d):
                 acc = 0.0
@@ -188,10 +198,10 @@ def test_fp8_close_to_unquantised():
 
 
 def test_row_maximum_over_all_keys_not_a_prefix():
-    # the reference maximum is the row's own over every key of its sequence: a row whose
-    # largest score is its LAST key still has that key at exactly 448 and every other weight
-    # quantised against it (computed here directly from the definition), whatever the
-    # number of keys before it
+    # the reference is the row's own maximum over every key of its sequence: a row whose
+    # largest score is its LAST key still has every weight quantised against that key's
+    # exponent (computed here directly from the definition), whatever the number of keys
+    # before it
     rng = np.random.default_rng(14)
     S = 300
     q8 = _codes(rng, (4, D), 2.0)
@@ -202,9 +212,54 @@ def test_row_maximum_over_all_keys_not_a_prefix():
     k8, v8, raw = k8[order], v8[order], raw[:, order]
     args = (0.02, 0.03, 0.004, 1 / math.sqrt(D))
     out, p8, L = oracle.fp8_attention_head(q8, k8, v8, *args, return_weights=True)
-    c = 0.02 * 0.03 / math.sqrt(D)
+    c = 0.02 * 0.03 / math.sqrt(D) / math.log(2.0)
     for r in range(4):
-        m = max(raw[r]) * c
-        want = [e4m3_encode(np.array([math.exp(x * c - m) * 448.0]))[0] for x in raw[r]]
+        M = math.ceil(max(raw[r]) * c)
+        want = [e4m3_encode(np.array([448.0 * 2.0 ** (x * c - M)]))[0] for x in raw[r]]
         assert list(p8[r]) == want, r
-    assert e4m3_decode(p8[0, -1:])[0] == 448.0
+    assert p8[0, -1] == p8[0].max() and e4m3_decode(p8[0, -1:])[0] >= 224.0
+
+
+def _one_pass(q8, k8, v8, sq, sk, sv, sigma, block=64):
+    """Blocks of keys in order, each block's weights E4M3(448 * 2^(t - M_run)) against the
+    running reference exponent M_run = ceil(running max of t), the partial sums multiplied
+    by 2^(M_old - M_new) whenever it grows (an independent evaluation of the rule)."""
+    q, k, v = e4m3_decode(q8), e4m3_decode(k8), e4m3_decode(v8)
+    t_all = (q @ k.T) * (sq * sk * sigma / math.log(2.0))
+    R = q.shape[0]
+    M = np.full(R, -np.inf)
+    acc = np.zeros((R, v.shape[1]))
+    L = np.zeros(R)
+    for j0 in range(0, k.shape[0], block):
+        t = t_all[:, j0:j0 + block]
+        Mn = np.maximum(M, np.ceil(t.max(axis=1)))
+        f = np.where(np.isfinite(M), np.exp2(M - Mn), 0.0)   # exact powers of two
+        acc *= f[:, None]
+        L *= f
+        p = e4m3_decode(e4m3_encode(448.0 * np.exp2(t - Mn[:, None])))
+        acc += p @ v[j0:j0 + block]
+        L += p.sum(axis=1)
+        M = Mn
+    return acc * sv / L[:, None]
+
+
+def test_one_pass_with_power_of_two_rescale_gives_the_rule():
+    # unit-variance rows keep every weight in E4M3's normal range, where the single pass
+    # and the definition agree to float64 rounding, however the running maximum grows
+    rng = np.random.default_rng(15)
+    for S in (64, 200, 1000):
+        q8 = _codes(rng, (32, D))
+        k8 = _codes(rng, (S, D))
+        v8 = _codes(rng, (S, D))
+        args = (0.008, 0.008, 0.02, 1 / math.sqrt(D))
+        want, p8, _ = oracle.fp8_attention_head(q8, k8, v8, *args, return_weights=True)
+        assert e4m3_decode(p8).min() >= 2.0 ** -6        # the premise: no subnormal weight
+        got = _one_pass(q8, k8, v8, *args)
+        assert np.allclose(got, want, rtol=1e-13, atol=1e-16), S
+        t = e4m3_decode(q8) @ e4m3_decode(k8).T * (0.008 * 0.008 / math.sqrt(D) / math.log(2.0))
+        if S > 64:   # the running reference did grow after the first block in some rows
+            assert np.any(np.ceil(t[:, :64].max(axis=1)) < np.ceil(t.max(axis=1)))
+        # with the exact maximum as the reference, the weights would differ
+        s = t * math.log(2.0)
+        exact_ref = e4m3_encode(448.0 * np.exp(s - s.max(axis=1, keepdims=True)))
+        assert not np.array_equal(exact_ref, p8)

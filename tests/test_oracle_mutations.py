@@ -94,8 +94,19 @@ CASES = [
      [("return float(np.max(np.abs(x)))", "return float(np.max(x))")],
      [lambda: TS.test_amax_vs_integer_bits(0)]),
     ("row maximum over the first 64 keys only", ATT,
-     [("m = np.max(s, axis=1, keepdims=True)", "m = np.max(s[:, :64], axis=1, keepdims=True)")],
+     [("M = np.ceil(np.max(t, axis=1, keepdims=True))",
+       "M = np.ceil(np.max(t[:, :64], axis=1, keepdims=True))")],
      [TA.test_weights_sum_to_one_and_key_permutation, TA.test_row_maximum_over_all_keys_not_a_prefix]),
+    ("reference exponent rounded down", ATT,
+     [("M = np.ceil(np.max(t, axis=1, keepdims=True))",
+       "M = np.floor(np.max(t, axis=1, keepdims=True))")],
+     [TA.test_worked_two_key_example, TA.test_weights_sum_to_one_and_key_permutation]),
+    ("exact row maximum as the reference", ATT,
+     [("M = np.ceil(np.max(t, axis=1, keepdims=True))", "M = np.max(t, axis=1, keepdims=True)")],
+     [TA.test_worked_two_key_example, TA.test_one_pass_with_power_of_two_rescale_gives_the_rule]),
+    ("natural exponential in place of base 2", ATT,
+     [("p_tilde = np.exp2(t - M)", "p_tilde = np.exp(t - M)")],
+     [TA.test_worked_two_key_example]),
     ("softmax scale dropped", ATT,
      [("        s = raw * c\n", "        s = raw * float(scale_q) * float(scale_k)\n")],
      [TA.test_worked_two_key_example]),
