@@ -5,48 +5,53 @@
 // 어텐션", "Requirements": varlen FP8 attention with per-tensor scales): for each packed
 // sequence i, head h and query row r, over the keys j of sequence i only,
 //   s_j  = (q8 . k8_j) * scale_q * scale_k * softmax_scale,
-//   m    = max_j s_j, the row maximum over ALL keys of the sequence,
-//   p8_j = E4M3(exp(s_j - m) * 448)          (fixed scale 448, so p8 <= 448),
+//   M    = ceil(m * log2 e), m = max_j s_j over ALL keys of the sequence,
+//   p8_j = E4M3(448 * 2^(s_j log2 e - M))     (the largest weight in [224, 448]),
 //   O    = scale_v * sum_j p8_j v8_j / sum_j p8_j, stored as bf16.
-// Every weight is quantised against the final row maximum, so the result does not depend
-// on how the keys are split into tiles. The kernel therefore makes two passes over a
-// row's keys: a max pass (score MFMAs and a running maximum only), then the main pass
-// (scores again, exp, E4M3 cast, PV), which needs no online rescale of O.
+// One pass over the keys: each tile's weights are taken against the running reference
+// exponent (the row maximum so far, in log2 units, rounded up), and when it grows the O
+// and row-sum accumulators are multiplied by 2^(old - new). Multiplying by a power of two
+// commutes with the E4M3 rounding while the weights stay at or above 2^-6, and is exact
+// on the fp32 accumulators, so the result is that of the final reference, independent of
+// the tiling; only weights that end below 2^-6 (keys more than ~10 nats under the row
+// maximum, seen before it) keep the finer rounding of their provisional reference: each
+// differs from its E4M3 code by at most 2^-9 on the weights' scale (where the largest
+// weight is 224 to 448).
 //
 // Mapping onto the matrix cores (v_mfma_f32_32x32x64_f8f6f4, fp32 accumulate):
 //   * a block owns 128 queries of one (sequence, head); each of its 4 waves owns 32;
 //   * scores are produced transposed, S^T = K Q^T, so that in the accumulator layout a
-//     lane holds ONE query (column l % 32) and 16 keys per 32x32 block: the row maximum
+//     lane holds ONE query (column l % 32) and 16 keys per 32x32 block; the row maximum
 //     is a per-lane reduction plus one v_permlane32_swap with the other lane half;
 //   * the K rows of a tile are stored in LDS in a permuted order so that lane half g
 //     ends up holding the 32 consecutive keys g*32 .. g*32+31 of the 64-key tile; the
 //     packed E4M3 probabilities are then directly the B operand of O^T = V^T P^T, and the
 //     A operand is 32 consecutive key bytes of one channel row of V8t (keys contiguous,
 //     as written by the quantise kernel) -- no LDS round trip for P;
+//   * O^T in the accumulator layout again puts one query per lane, so the rescale is a
+//     per-lane multiply by a power of two; it is skipped for the whole wave when no
+//     lane's reference exponent grew (after the first tiles, almost always);
 //   * the row sum of the quantised weights accumulates on the matrix core (one extra MFMA
-//     with an all-ones A operand per tile).
+//     with an all-ones A operand per tile, into a running accumulator rescaled with O).
 //
-// Schedule. At d = 128 the vector ALU, not the matrix core, bounds the main pass: per
-// score it needs one FMA, one v_exp_f32 (about 2.3 FMA slots) and half a
-// v_cvt_pk_fp8_f32 (about 1.7 slots), and every MFMA issue blocks the ALU for a few
-// cycles; the max pass is matrix-core work (4 of the 9 MFMAs of a main-pass tile, and a
-// v_max3 per two scores). Keeping both pipes busy takes a software pipeline inside each
-// wave plus two waves per SIMD:
-//   * main pass, iteration t: the exp/convert of tile t on the vector ALU while the
-//     matrix core runs PV of tile t-1 and the scores of tile t+1; the region is written in
-//     issue order (each MFMA followed by one chunk of 4 scores, sched_barrier between
-//     pairs), and the new P is pinned before the loop back edge;
-//   * max pass, iteration u: the scores of tile u+1 on the matrix core while the vector
-//     ALU takes the maximum of tile u; its last iteration already computes the scores of
-//     the main pass's first tile;
-//   * one stream of K tiles (the max pass's n tiles, then the main pass's n again) and
-//     one of V8t tiles go global -> LDS with buffer loads that write LDS directly (no VGPR
-//     staging, no ds_write), in four-stage rings; tiles move in pairs, with one vmcnt
-//     wait and one barrier per pair of iterations, each pair's loads issued one pair ahead
-//     of use, across the boundary between the passes; 16-byte LDS chunks are XOR-swizzled
-//     so operand reads are conflict-free; the ragged last tile is masked only in the last
-//     iteration of each pass;
-//   * exp(s - m) * 448 is computed as exp2(s * c - (m * c - log2 448)), c = scales *
+// Schedule. At d = 128 the vector ALU, not the matrix core, bounds this kernel: per score
+// it needs one FMA, one v_exp_f32 (about 2.3 FMA slots), half a v_cvt_pk_fp8_f32 (about
+// 1.7 slots) and part of a v_max3, and every MFMA issue blocks the ALU for a few cycles;
+// the matrix core needs 1/4 of a 32x32x64 MFMA slot per 64 scores. Keeping both busy
+// takes a software pipeline inside each wave plus two waves per SIMD:
+//   * iteration t runs the softmax of tile t on the vector ALU while the matrix core runs
+//     PV of tile t-1 and the scores of tile t+1; the MFMAs are spread through the VALU
+//     stream (sched_barrier), and the new P is pinned before the loop back edge so the
+//     compiler cannot sink its exp/convert chain past the next tile's rescale branch;
+//   * the rescale for tile t-1's reference runs at the top of iteration t, after PV(t-2)
+//     was issued and before PV(t-1) is;
+//   * the loop is unrolled by two so the two score register sets swap roles without
+//     copies; a ragged last tile is handled (masked) only in the epilogue;
+//   * K and V8t tiles go global -> LDS with buffer loads that write LDS directly (no VGPR
+//     staging, no ds_write), in four-stage rings; tiles move in pairs, with one vmcnt wait
+//     and one barrier per pair of tiles, each pair's loads issued one pair ahead of use;
+//     16-byte LDS chunks are XOR-swizzled so operand reads are conflict-free;
+//   * 448 * 2^(s log2 e - M) is computed as exp2(s * c - (M - log2 448)), c = scales *
 //     log2(e): one FMA and one v_exp_f32 per score;
 //   * block -> work mapping is XCD-aware: consecutive work units (the q-tiles of one head,
 //     sequence after sequence) go to the same XCD so its L2 keeps that head's K/V; units
@@ -61,11 +66,9 @@ namespace fp8attn {
 
 namespace {
 
-constexpr int kWaves = 4;                // waves per block, 32 queries each
-constexpr int kBM = 32 * kWaves;         // queries per block
+constexpr int kBM = 128;                 // queries per block
 constexpr int kBN = 64;                  // keys per tile
-constexpr int kThreads = 64 * kWaves;
-constexpr int kLoadsPerTile = 8 / kWaves;   // 1 KB load instructions per wave per tile
+constexpr int kThreads = 256;
 constexpr int kKTileBytes = kBN * kHeadDim;   // K tile: 64 rows x 128 B
 constexpr int kVTileBytes = kHeadDim * kBN;   // V8t tile: 128 rows x 64 B
 constexpr int kStages = 4;                    // ring depth of each of K and V8t
@@ -145,24 +148,23 @@ __device__ __forceinline__ int quant4(const v16f& s, int i0, float c, float mc) 
                            fast_exp2(__builtin_fmaf(s[i0 + 3], c, -mc)), w);
 }
 
-// Running maximum of this lane's query over its 32 keys of one tile (keys g*32 + i in s0,
-// g*32 + 16 + i in s1); keys at or past key_lim are left out when MASK. Two independent
-// chains (the compiler folds each into v_max3).
+// Row maximum of this lane's query over one tile of scores (both lane halves). Masked
+// keys (g*32 + i, g*32 + 16 + i at or past key_lim) are left out.
 template <bool MASK>
-__device__ __forceinline__ float lane_tile_max(const v16f& s0, const v16f& s1, int g, int key_lim,
-                                               float run) {
+__device__ __forceinline__ float tile_max(const v16f& s0, const v16f& s1, int g, int key_lim) {
   auto val = [&](const v16f& s, int i, int key) __attribute__((always_inline)) {
     return (MASK && key >= key_lim) ? -__builtin_inff() : s[i];
   };
-  float m0 = run, m1 = val(s1, 0, g * 32 + 16);
+  // one running chain (the compiler folds it into v_max3 without re-quieting every input)
+  float mx = __builtin_fmaxf(val(s0, 0, g * 32), val(s0, 1, g * 32 + 1));
 #pragma unroll
-  for (int i = 0; i < 16; ++i) m0 = __builtin_fmaxf(m0, val(s0, i, g * 32 + i));
+  for (int i = 2; i < 16; ++i) mx = __builtin_fmaxf(mx, val(s0, i, g * 32 + i));
 #pragma unroll
-  for (int i = 1; i < 16; ++i) m1 = __builtin_fmaxf(m1, val(s1, i, g * 32 + 16 + i));
-  return __builtin_fmaxf(m0, m1);
+  for (int i = 0; i < 16; ++i) mx = __builtin_fmaxf(mx, val(s1, i, g * 32 + 16 + i));
+  return half_swap_max(mx);
 }
 
-// p = exp(s - m) * 448 = exp2(s*c - mc), mc = m*c - log2 448; packed E4M3 with byte j of
+// p = 448 * 2^(s*c - M) = exp2(s*c - mc), mc = M - log2 448; packed E4M3 with byte j of
 // the 32 = key g*32 + j of the tile. Masked keys get exp2(-inf) = 0 (the exponent
 // argument, not the score, is replaced, so a zero c cannot make -inf * 0).
 template <bool MASK>
@@ -240,15 +242,15 @@ void attn_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__
   // 1 KB of LDS with lane L at byte 16 L, so each lane fetches the global chunk that
   // belongs at its LDS position: K block b (8 rows of 128 B) row R = 8b + L/8, physical
   // chunk L % 8 = logical chunk ^ k_swz(R), key = the key stored at row R; V8t block b
-  // (16 rows of 64 B) row R = 16b + L/4, chunk L % 4 = logical ^ v_swz(R). Wave w loads
-  // blocks kLoadsPerTile * w + j of each tile.
+  // (16 rows of 64 B) row R = 16b + L/4, chunk L % 4 = logical ^ v_swz(R). Each of the
+  // 4 waves loads blocks 2w and 2w + 1 of each tile.
   const uint8_t* kbase = k8 + (int64_t)seq_begin * row_stride + head * kHeadDim;
   const uint8_t* vbase = v8t + (int64_t)head * kHeadDim * Tp + pad_start(seq_begin, seq);
   const int wv = __builtin_amdgcn_readfirstlane(wave);
-  int kvo[kLoadsPerTile], vvo[kLoadsPerTile];
+  int kvo[2], vvo[2];
 #pragma unroll
-  for (int j = 0; j < kLoadsPerTile; ++j) {
-    const int b = kLoadsPerTile * wv + j;
+  for (int j = 0; j < 2; ++j) {
+    const int b = 2 * wv + j;
     const int R = 8 * b + (lane >> 3);
     const int kb = R >> 5, m = R & 31;
     const int key = ((m >> 2) & 1) * 32 + kb * 16 + (m >> 3) * 4 + (m & 3);   // inverse of k_lds_row
@@ -256,46 +258,48 @@ void attn_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__
     const int RV = 16 * b + (lane >> 2);
     vvo[j] = RV * (int)Tp + (((lane & 3) ^ v_swz(RV)) << 4);
   }
+  const int kvo0 = kvo[0], kvo1 = kvo[1], vvo0 = vvo[0], vvo1 = vvo[1];
   typedef __attribute__((address_space(3))) void lds_void;
   uint8_t* const kst = smem;                                // K stage i at kst + i * kKTileBytes
   uint8_t* const vst = smem + kStages * kKTileBytes;        // V stage i at vst + i * kVTileBytes
-  const int n = (S + kBN - 1) / kBN;                        // key tiles of the sequence
-  // K tile j into LDS at dst; rows at or past the end of the sequence read as 0 (a tile
-  // wholly past the end, as the max pass's odd last pair may ask for, reads all zeros)
-  auto load_k_to = [&](int j, uint8_t* dst) __attribute__((always_inline)) {
-    const int k0 = j * kBN;
-    // uniform by construction; readfirstlane keeps it in SGPRs (a saturating subtract on
-    // the vector ALU would make the compiler wrap the load in a waterfall loop)
-    const int rows = __builtin_amdgcn_readfirstlane(S - k0 > 0 ? S - k0 : 0);
-    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(kbase + (int64_t)(rows > 0 ? k0 : 0) * row_stride), (short)0, rows * row_stride,
-        kBufferFlags);
-    dst += wv * (kLoadsPerTile * 1024);
-#pragma unroll
-    for (int jj = 0; jj < kLoadsPerTile; ++jj)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(dst + jj * 1024), 16, kvo[jj], 0,
-                                               0, 0);
-  };
-  // main pass: K tile j into K-ring stage j % 4 (clamped to the last tile, so the loads
-  // past the end stay in bounds; they fill stages that are never read again)
+  const int ntiles = (S + kBN - 1) / kBN;
+  // K tile j into stage j % 4 (clamped to the last tile, so the loads past the end stay in
+  // bounds; they fill stages that are never read again); rows at or past the end of the
+  // sequence read as 0
   auto load_k = [&](int j) __attribute__((always_inline)) {
-    load_k_to(j < n ? j : n - 1, kst + (j & (kStages - 1)) * kKTileBytes);
+    const int stage = j & (kStages - 1);
+    const int k0 = (j < ntiles ? j : ntiles - 1) * kBN;
+    // uniform by construction; readfirstlane keeps it in SGPRs (a vector value would make
+    // the compiler wrap the load in a waterfall loop)
+    const int rows = __builtin_amdgcn_readfirstlane(S - k0);
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(kbase + (int64_t)k0 * row_stride), (short)0, rows * row_stride, kBufferFlags);
+    uint8_t* dst = kst + stage * kKTileBytes + wv * 2048;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)dst, 16, kvo0, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(dst + 1024), 16, kvo1, 0, 0, 0);
   };
   // V8t tile j into stage j % 4 (clamped like K): columns up to the sequence's 128-aligned
   // padded length, which the quantise kernel zero-fills
   auto load_v = [&](int j) __attribute__((always_inline)) {
     const int stage = j & (kStages - 1);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(vbase + (j < n ? j : n - 1) * kBN), (short)0, 0x7fffffff, kBufferFlags);
-    uint8_t* dst = vst + stage * kVTileBytes + wv * (kLoadsPerTile * 1024);
-#pragma unroll
-    for (int jj = 0; jj < kLoadsPerTile; ++jj)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(dst + jj * 1024), 16, vvo[jj], 0,
-                                               0, 0);
+        (void*)(vbase + (j < ntiles ? j : ntiles - 1) * kBN), (short)0, 0x7fffffff,
+        kBufferFlags);
+    uint8_t* dst = vst + stage * kVTileBytes + wv * 2048;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)dst, 16, vvo0, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(dst + 1024), 16, vvo1, 0, 0, 0);
   };
 
-  // ---- Q^T operand (B of S^T = K Q^T): lane = query n, 32 channel bytes of half g.
-  // Issued before any tile load, so that the first partial vmcnt wait also covers it.
+  // ---- prologue loads: everything iteration 0 and the first pair (tiles 1, 2) read:
+  // K(0) .. K(3), V(0), V(1). Tile j always lives in stage j % 4 of its ring.
+  load_k(0);
+  load_k(1);
+  load_k(2);
+  load_k(3);
+  load_v(0);
+  load_v(1);
+
+  // ---- Q^T operand (B of S^T = K Q^T): lane = query n, 32 channel bytes of half g
   const int q_local = qt * kBM + wave * 32 + ln.n;
   const int q_row = seq_begin + (q_local < S ? q_local : S - 1);
   const uint8_t* qp = q8 + (int64_t)q_row * row_stride + head * kHeadDim;
@@ -316,85 +320,42 @@ void attn_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__
     ln.vs1 = ((ln.g * 2 + 1) ^ sv) << 4;
   }
 
-  // ==== max pass. The whole 64 KB of LDS is one ring of 8 K stages; pair i = tiles 2i,
-  // 2i+1 in stages (2i) % 8, (2i+1) % 8. Iteration i: wait for pair i (pairs i+1, i+2 may
-  // still be in flight: a partial vmcnt wait), barrier, issue pair i+3 into the stages of
-  // pair i-1 (read by iteration i-1, before the barrier), scores of pair i on the matrix
-  // core while the vector ALU takes the maximum over pair i-1.
-  const int npairs = (n + 1) / 2;
-  auto load_pair = [&](int i) __attribute__((always_inline)) {
-    load_k_to(2 * i, smem + ((2 * i) & 7) * kKTileBytes);
-    load_k_to(2 * i + 1, smem + ((2 * i + 1) & 7) * kKTileBytes);
-  };
-  load_pair(0);
-  if (npairs > 1) load_pair(1);
-  if (npairs > 2) load_pair(2);
-  float mx = -__builtin_inff();   // running maximum of this lane's scores
-  // scores of one pair in two register sets that swap roles from one iteration to the
-  // next (the loop is unrolled by two, so no copies): tile 2i in x0, x1, tile 2i+1 in x2, x3
-  v16f sa0, sa1, sa2, sa3, sb0, sb1, sb2, sb3;
-  auto max_iteration = [&](int i, v16f& c0, v16f& c1, v16f& c2, v16f& c3, v16f& n0, v16f& n1,
-                           v16f& n2, v16f& n3) __attribute__((always_inline)) {
-    // pairs issued after pair i: min(2, npairs - 1 - i), 2 * kLoadsPerTile loads each
-    if (i + 2 < npairs) {
-      loads_barrier<4 * kLoadsPerTile>();
-    } else if (i + 1 < npairs) {
-      loads_barrier<2 * kLoadsPerTile>();
-    } else {
-      loads_barrier<0>();
-    }
-    if (i + 3 < npairs) load_pair(i + 3);
-    scores(smem + ((2 * i) & 7) * kKTileBytes, ln, qb0, qb1, n0, n1);
-    scores(smem + ((2 * i + 1) & 7) * kKTileBytes, ln, qb0, qb1, n2, n3);
-    if (i > 0) {
-      mx = lane_tile_max<false>(c0, c1, ln.g, kBN, mx);
-      mx = lane_tile_max<false>(c2, c3, ln.g, kBN, mx);
-    }
-  };
-  int i = 0;
-  for (; i + 1 < npairs; i += 2) {
-    max_iteration(i, sb0, sb1, sb2, sb3, sa0, sa1, sa2, sa3);
-    max_iteration(i + 1, sa0, sa1, sa2, sa3, sb0, sb1, sb2, sb3);
-  }
-  if (i < npairs) {
-    max_iteration(i, sb0, sb1, sb2, sb3, sa0, sa1, sa2, sa3);
-  } else {
-    sa0 = sb0;   // once per block: the last pair's scores into set a
-    sa1 = sb1;
-    sa2 = sb2;
-    sa3 = sb3;
-  }
-  {
-    // the last pair: keys at or past the end of the sequence are left out
-    const int lim = S - 2 * (npairs - 1) * kBN;   // 1 .. 128 valid keys in the pair
-    mx = lane_tile_max<true>(sa0, sa1, ln.g, lim, mx);
-    mx = lane_tile_max<true>(sa2, sa3, ln.g, lim - kBN, mx);
-  }
-  // the row maximum (both lane halves); the weights are exp2(s * c - mc)
-  const float mc = half_swap_max(mx) * c - kLog2E4M3Max;
-
-  // ==== main pass. Every wave is done with the max pass's LDS (the barrier), which now
-  // becomes a ring of 4 K stages and one of 4 V8t stages.
-  asm volatile("s_barrier" ::: "memory");
-  load_k(0);
-  load_k(1);
-  load_k(2);
-  load_k(3);
-  load_v(0);
-  load_v(1);
-
+  // ---- per-lane state for query n
+  // ref_prev: reference exponent (the running row maximum in log2 units, rounded up to an
+  // integer) after the last tile whose softmax ran; ref_acc: the exponent that the O and
+  // row-sum accumulators are relative to (they catch up at the top of each iteration,
+  // before the pending PV is issued, so the rescale never sits between the softmax and the
+  // MFMAs it overlaps). Both hold integers (as floats) or -inf before the first tile.
+  float ref_prev = -__builtin_inff();
+  float ref_acc = -__builtin_inff();
   v16f o0 = {}, o1 = {}, o2 = {}, o3 = {};
   v16f rs = {};                                         // row sum of P (entry 0 is used)
   v8i ones;
 #pragma unroll
   for (int r = 0; r < 8; ++r) ones[r] = (int)kOnesE4M3;
   asm volatile("" : "+v"(ones));   // opaque: kept in registers, not rebuilt every tile
-  const int last_lim = S - (n - 1) * kBN;               // valid keys of the last tile
+  const int last_lim = S - (ntiles - 1) * kBN;          // valid keys of the last tile
+  v16f sa0, sa1, sb0, sb1;                              // two score register sets
   v8i p_prev;                                           // quantised P of the previous tile
 
-  // ---- scores of tile 0
+  // ---- scores of tile 0. The Q loads are younger than the prologue's tile loads and are
+  // counted by vmcnt too: wait for everything once here.
   loads_barrier<0>();
   scores(kst, ln, qb0, qb1, sa0, sa1);
+
+  auto catch_up = [&]() __attribute__((always_inline)) {
+    if (wave_any(ref_prev > ref_acc)) {
+      // an exact power of two, 2^(ref_acc - ref_prev); 0 while ref_acc = -inf (the clamp
+      // keeps the conversion to int defined)
+      const float alpha = __builtin_ldexpf(1.0f, (int)__builtin_fmaxf(ref_acc - ref_prev, -200.0f));
+      rs[0] *= alpha;
+      o0 *= alpha;
+      o1 *= alpha;
+      o2 *= alpha;
+      o3 *= alpha;
+    }
+    ref_acc = ref_prev;
+  };
 
   // Synchronisation of a pair of iterations t, t+1 (t odd). They read K(t+1), K(t+2),
   // V(t-1), V(t), all loaded by the previous pair (or the prologue): wait for this
@@ -409,17 +370,18 @@ void attn_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__
     load_v(t + 2);
   };
 
-  // Iteration t < n - 1: exp/convert of tile t (scores in cur), scores of tile t+1 into
+  // Iteration t < ntiles - 1: softmax of tile t (scores in cur), scores of tile t+1 into
   // nxt, PV of tile t-1 (when t > 0).
   auto iteration = [&](int t, v16f& cur0, v16f& cur1, v16f& nxt0, v16f& nxt1,
                        auto do_pv) __attribute__((always_inline)) {
     constexpr bool PV = decltype(do_pv)::value;
     const int sk = (t + 1) & (kStages - 1);     // stage of K(t+1)
     const int sv = (t - 1) & (kStages - 1);     // stage of V(t-1)
-    // ---- one region, written in issue order: each MFMA is followed by one chunk of 4
-    // scores' exp and convert, and sched_barrier(0) keeps every pair where it is, so the
-    // matrix core always has the next MFMA queued while the vector ALU works through the
-    // chunk.
+    if (PV) catch_up();
+    // ---- one region, written in issue order: each MFMA is followed by one chunk of the
+    // softmax (a part of the row maximum, or the exp/convert of 4 scores), and
+    // sched_barrier(0) keeps every pair where it is, so the matrix core always has the
+    // next MFMA queued while the vector ALU works through the chunk.
     const uint8_t* vr = vst + sv * kVTileBytes + ln.n * kBN;        // V(t-1) row of lane
     const uint8_t* kr0 = kst + sk * kKTileBytes + ln.n * kHeadDim;  // K(t+1) rows of lane
     const uint8_t* kr1 = kr0 + 32 * kHeadDim;
@@ -432,57 +394,66 @@ void attn_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__
       va3 = load32(vr + 96 * kBN + ln.vs0, vr + 96 * kBN + ln.vs1);
     }
     __builtin_amdgcn_sched_barrier(0);
-    v8i p;
     if (PV) rs = mfma_e4m3_32x32x64(ones, p_prev, rs);
-    p[0] = quant4(cur0, 0, c, mc);
+    float mx = __builtin_fmaxf(cur0[0], cur0[1]);
+#pragma unroll
+    for (int i = 2; i < 16; ++i) mx = __builtin_fmaxf(mx, cur0[i]);
     __builtin_amdgcn_sched_barrier(0);
     if (PV) o0 = mfma_e4m3_32x32x64(va0, p_prev, o0);
-    // the K operands of tile t+1 (read after va0 is consumed: fewer live registers)
     const v8i ka0 = load32(kr0 + ln.ks00, kr0 + ln.ks01);
     const v8i kb0 = load32(kr1 + ln.ks00, kr1 + ln.ks01);
     const v8i ka1 = load32(kr0 + ln.ks10, kr0 + ln.ks11);
     const v8i kb1 = load32(kr1 + ln.ks10, kr1 + ln.ks11);
-    p[1] = quant4(cur0, 4, c, mc);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = __builtin_fmaxf(mx, cur1[i]);
+    // c > 0, so the maximum of the raw dot products gives the maximum score
+    const float ref_cur = __builtin_fmaxf(ref_prev, __builtin_ceilf(half_swap_max(mx) * c));
+    const float mc = ref_cur - kLog2E4M3Max;
     __builtin_amdgcn_sched_barrier(0);
+    v8i p;
     if (PV) o1 = mfma_e4m3_32x32x64(va1, p_prev, o1);
-    p[2] = quant4(cur0, 8, c, mc);
+    p[0] = quant4(cur0, 0, c, mc);
     __builtin_amdgcn_sched_barrier(0);
     if (PV) o2 = mfma_e4m3_32x32x64(va2, p_prev, o2);
-    p[3] = quant4(cur0, 12, c, mc);
+    p[1] = quant4(cur0, 4, c, mc);
     __builtin_amdgcn_sched_barrier(0);
     if (PV) o3 = mfma_e4m3_32x32x64(va3, p_prev, o3);
-    p[4] = quant4(cur1, 0, c, mc);
+    p[2] = quant4(cur0, 8, c, mc);
     __builtin_amdgcn_sched_barrier(0);
     nxt0 = mfma_e4m3_32x32x64(ka0, qb0, zero16);
-    p[5] = quant4(cur1, 4, c, mc);
+    p[3] = quant4(cur0, 12, c, mc);
     __builtin_amdgcn_sched_barrier(0);
     nxt1 = mfma_e4m3_32x32x64(kb0, qb0, zero16);
-    p[6] = quant4(cur1, 8, c, mc);
+    p[4] = quant4(cur1, 0, c, mc);
     __builtin_amdgcn_sched_barrier(0);
     nxt0 = mfma_e4m3_32x32x64(ka1, qb1, nxt0);
-    p[7] = quant4(cur1, 12, c, mc);
+    p[5] = quant4(cur1, 4, c, mc);
     __builtin_amdgcn_sched_barrier(0);
     nxt1 = mfma_e4m3_32x32x64(kb1, qb1, nxt1);
+    p[6] = quant4(cur1, 8, c, mc);
+    __builtin_amdgcn_sched_barrier(0);
+    p[7] = quant4(cur1, 12, c, mc);
     pin(p);
     p_prev = p;
+    ref_prev = ref_cur;
   };
   using T_ = std::true_type;
   using F_ = std::false_type;
 
-  // ---- main loop over t = 0 .. n-2 in pairs (scores alternate a <-> b). Iteration 0
-  // reads only prologue tiles, which the barrier above published.
+  // ---- main loop over t = 0 .. ntiles-2 in pairs (scores alternate a <-> b). Iteration
+  // 0 reads only prologue tiles, which the barrier above published.
   int t = 0;
-  if (n > 1) {
+  if (ntiles > 1) {
     iteration(0, sa0, sa1, sb0, sb1, F_{});
     t = 1;
-    for (; t + 2 < n; t += 2) {
+    for (; t + 2 < ntiles; t += 2) {
       pair_sync(t);
       iteration(t, sb0, sb1, sa0, sa1, T_{});
       iteration(t + 1, sa0, sa1, sb0, sb1, T_{});
     }
-    if (t + 1 < n) {
-      // a last single iteration t = n - 2: K(t+1), V(t-1) came with the previous pair;
-      // V(t+1) = V(n-1) is still to load (for the epilogue)
+    if (t + 1 < ntiles) {
+      // a last single iteration t = ntiles - 2: K(t+1), V(t-1) came with the previous
+      // pair; V(t+1) = V(ntiles-1) is still to load (for the epilogue)
       loads_barrier<0>();
       load_v(t + 1);
       iteration(t, sb0, sb1, sa0, sa1, T_{});
@@ -492,13 +463,26 @@ void attn_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__
       sa1 = sb1;
     }
   }
-  // ---- epilogue: t = n - 1, scores in set a; V(n-2), V(n-1) loaded
+  // ---- epilogue: t = ntiles - 1, scores in set a; V(ntiles-2), V(ntiles-1) loaded
   loads_barrier<0>();
-  if (n > 1)
-    pv(vst + ((n - 2) & (kStages - 1)) * kVTileBytes, ln, p_prev, ones, rs, o0, o1, o2, o3);
-  p_prev = last_lim != kBN ? quantise_p<true>(sa0, sa1, c, mc, ln.g, last_lim)
-                           : quantise_p<false>(sa0, sa1, c, mc, ln.g, kBN);
-  pv(vst + ((n - 1) & (kStages - 1)) * kVTileBytes, ln, p_prev, ones, rs, o0, o1, o2, o3);
+  if (ntiles > 1) {
+    catch_up();
+    pv(vst + ((ntiles - 2) & (kStages - 1)) * kVTileBytes, ln, p_prev, ones, rs, o0, o1, o2,
+       o3);   // PV(ntiles-2)
+  }
+  {
+    const bool ragged = last_lim != kBN;
+    const float ref_cur = __builtin_fmaxf(
+        ref_prev, __builtin_ceilf(c * (ragged ? tile_max<true>(sa0, sa1, ln.g, last_lim)
+                                              : tile_max<false>(sa0, sa1, ln.g, kBN))));
+    const float mc = ref_cur - kLog2E4M3Max;
+    p_prev = ragged ? quantise_p<true>(sa0, sa1, c, mc, ln.g, last_lim)
+                    : quantise_p<false>(sa0, sa1, c, mc, ln.g, kBN);
+    ref_prev = ref_cur;
+  }
+  catch_up();
+  pv(vst + ((ntiles - 1) & (kStages - 1)) * kVTileBytes, ln, p_prev, ones, rs, o0, o1, o2,
+     o3);   // PV(ntiles-1)
 
   // ---- O = O * scale_v / l, bf16, one query row per lane
   if (q_local < S) {
@@ -531,8 +515,7 @@ void attn_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__
 hipError_t launch_attn_fp8(const AttnLaunch& a, const fp8attn_state* st, const uint8_t* q8,
                            const uint8_t* k8, const uint8_t* v8t, hipStream_t s) {
   if (a.max_seqlen <= 0) return hipSuccess;
-  static_assert(kBM == 128, "virtual tiles are 128 queries");
-  const int64_t vtiles = (a.T + 127) / 128 + a.num_seqs;   // per head, see vtile_start
+  const int64_t vtiles = (a.T + 127) / 128 + a.num_seqs;
   const int64_t units = vtiles * a.H;
   const int64_t per_xcd = (units + 7) / 8;
   if (per_xcd * 8 > 0x7fffffff) return hipErrorInvalidValue;

@@ -211,11 +211,15 @@ int fp8attn_attend(const void* state, const int32_t* cu_seqlens, const int32_t* 
  *   O[r,h,:] = sum_j w_j V[j,h,:] over the keys j of sequence i only.
  * FP8 path (flags without FP8ATTN_SKIP): quantises Q, K, V with the state's scales into
  *   `workspace` (see fp8attn_workspace_bytes), then s_j = (q8.k8_j) * scale_q * scale_k *
- *   softmax_scale; with m = max_j s_j, the row maximum over all keys of the sequence,
- *   p8_j = E4M3(exp(s_j - m) * 448) (fixed scale 448, so p8_j <= 448); O = scale_v *
- *   sum_j p8_j v8_j / sum_j p8_j. The PV product uses the E4M3 V; accumulation and softmax
- *   are fp32 (the scores and products on FP8 matrix cores); O is bf16. The result does not
- *   depend on how the kernel tiles the keys.
+ *   softmax_scale; with m = max_j s_j, the row maximum over all keys of the sequence, and
+ *   M = ceil(m * log2 e), p8_j = E4M3(448 * 2^(s_j * log2 e - M)) (448 times a power of
+ *   two, so the largest p8_j is in [224, 448]); O = scale_v * sum_j p8_j v8_j / sum_j p8_j.
+ *   The PV product uses the E4M3 V; accumulation and softmax are fp32 (the scores and
+ *   products on FP8 matrix cores); O is bf16. The kernel finds M in the same pass as the
+ *   weights (rescaling by powers of two as it grows), which gives this result whatever
+ *   the key tiling, except that a weight below 2^-6 of a key visited before the row's
+ *   final M keeps the finer rounding of its provisional reference (at most 2^-9 apart on
+ *   the weights' scale, where the largest weight is 224 to 448).
  *   Requires a preceding fp8attn_scales on this state (same stream), unless
  *   FP8ATTN_OBSERVE is set: then the call itself performs the dynamic observe + ring +
  *   scales update (fp8attn_quantize_dynamic) before the attention, writing the state.

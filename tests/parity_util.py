@@ -22,11 +22,14 @@ MEAN_ABS_TOL = 2e-3
 # within its hardware bound (hw_bound_rows): the matrix core's accumulation error can move a
 # single E4M3 weight across a rounding midpoint, which on a short row moves the output by
 # more than the stated tolerance; the cap keeps the bound from absorbing any number of such
-# elements. The error is relative to the largest product of a score, so it, and the number
-# of moved weights, grow with outlier channels:
-#   unit-variance inputs (the regime the stated tolerance is for): 1e-4 (measured: at most
-#   2.1e-6, on rows of fewer than 200 keys);
-#   inputs with x20 outlier channels: 5e-3 (measured: at most 1.6e-3, rows of 77-300 keys).
+# elements. Every weight, the largest included (448 times a power of two, not 448 itself),
+# sits on the E4M3 grid wherever the score puts it, so any of them can be moved. The error
+# is relative to the largest product of a score, so it, and the number of moved weights,
+# grow with outlier channels and with the softmax scale:
+#   unit-variance inputs at the default scale (the regime the stated tolerance is for):
+#   1e-4 (measured: at most 5.8e-5, on a batch of rows of 1 to 513 keys);
+#   inputs with x20 outlier channels, or a softmax scale 3.4 x the default: 5e-3
+#   (measured: at most 1.8e-3).
 OVER_TOL_CAP = 1e-4
 OVER_TOL_CAP_OUTLIERS = 5e-3
 # keys per FP8 MFMA of the PV and row-sum products (the K dimension of one instruction):
