@@ -9,14 +9,16 @@
 //   p8_j = E4M3(448 * 2^(s_j log2 e - M))     (the largest weight in [224, 448]),
 //   O    = scale_v * sum_j p8_j v8_j / sum_j p8_j, stored as bf16.
 // One pass over the keys: each tile's weights are taken against the running reference
-// exponent (the row maximum so far, in log2 units, rounded up), and when it grows the O
-// and row-sum accumulators are multiplied by 2^(old - new). Multiplying by a power of two
-// commutes with the E4M3 rounding while the weights stay at or above 2^-6, and is exact
-// on the fp32 accumulators, so the result is that of the final reference, independent of
-// the tiling; only weights that end below 2^-6 (keys more than ~10 nats under the row
-// maximum, seen before it) keep the finer rounding of their provisional reference: each
-// differs from its E4M3 code by at most 2^-9 on the weights' scale (where the largest
-// weight is 224 to 448).
+// exponent R_t (the row maximum so far, in log2 units, rounded up), and their PV and
+// row-sum products enter the accumulators multiplied by 2^(R_t - R_0) -- the MFMA's E8M0
+// scale on the P operand -- so the accumulators keep the first tile's reference R_0 and
+// are never rescaled (unless the shift would pass 2^64). Multiplying by a power of two
+// commutes with the E4M3 rounding while the weights stay at or above 2^-6, and is exact in
+// the fp32 products and sums, so O = sum / row sum is the result of the final reference,
+// independent of the tiling; only weights that end below 2^-6 (keys more than ~10 nats
+// under the row maximum, seen before it) keep the finer rounding of their provisional
+// reference: each differs from its E4M3 code by at most 2^-9 on the weights' scale (where
+// the largest weight is 224 to 448).
 //
 // Mapping onto the matrix cores (v_mfma_f32_32x32x64_f8f6f4, fp32 accumulate):
 //   * a block owns 128 queries of one (sequence, head); each of its 4 waves owns 32;
@@ -28,11 +30,11 @@
 //     packed E4M3 probabilities are then directly the B operand of O^T = V^T P^T, and the
 //     A operand is 32 consecutive key bytes of one channel row of V8t (keys contiguous,
 //     as written by the quantise kernel) -- no LDS round trip for P;
-//   * O^T in the accumulator layout again puts one query per lane, so the rescale is a
-//     per-lane multiply by a power of two; it is skipped for the whole wave when no
-//     lane's reference exponent grew (after the first tiles, almost always);
+//   * the B operand P^T holds one query per lane, so the per-query shift 2^(R_t - R_0) is
+//     the per-lane B scale of v_mfma_scale_f32_32x32x64_f8f6f4 (E8M0 in byte 0 of a VGPR;
+//     the B scale of lane l applies to its column l % 32 and key half l / 32);
 //   * the row sum of the quantised weights accumulates on the matrix core (one extra MFMA
-//     with an all-ones A operand per tile, into a running accumulator rescaled with O).
+//     with an all-ones A operand per tile, scaled like the PV products).
 //
 // Schedule. At d = 128 the vector ALU, not the matrix core, bounds this kernel: per score
 // it needs one FMA, one v_exp_f32 (about 2.3 FMA slots), half a v_cvt_pk_fp8_f32 (about
@@ -43,10 +45,12 @@
 //     PV of tile t-1 and the scores of tile t+1; the MFMAs are spread through the VALU
 //     stream (sched_barrier), and the new P is pinned before the loop back edge so the
 //     compiler cannot sink its exp/convert chain past the next tile's rescale branch;
-//   * the rescale for tile t-1's reference runs at the top of iteration t, after PV(t-2)
-//     was issued and before PV(t-1) is;
-//   * the loop is unrolled by two so the two score register sets swap roles without
-//     copies; a ragged last tile is handled (masked) only in the epilogue;
+//   * the loop is unrolled by four (two pairs of tiles): the two score register sets swap
+//     roles without copies, and every LDS ring stage the operand reads use is a constant
+//     (an immediate offset, no address arithmetic per tile); a ragged last tile is handled
+//     (masked) only in the epilogue;
+//   * the row maximum is a chain of v_max3 written as the instruction itself (fmaxf would
+//     make the compiler quiet every score first; scores are never NaN);
 //   * K and V8t tiles go global -> LDS with buffer loads that write LDS directly (no VGPR
 //     staging, no ds_write), in four-stage rings; tiles move in pairs, with one vmcnt wait
 //     and one barrier per pair of tiles, each pair's loads issued one pair ahead of use;
@@ -74,6 +78,9 @@ constexpr int kVTileBytes = kHeadDim * kBN;   // V8t tile: 128 rows x 64 B
 constexpr int kStages = 4;                    // ring depth of each of K and V8t
 constexpr uint32_t kOnesE4M3 = 0x38383838u;   // four E4M3 1.0
 constexpr int kBufferFlags = 0x00020000;      // raw buffer resource, dword 3 (gfx9)
+// largest exponent shift applied through the MFMA B scale before the accumulators are
+// rescaled: 2^64 x (448 x 448 x 2^20 keys) stays far below the fp32 range
+constexpr float kMaxShift = 64.0f;
 
 // LDS row of key kappa (0..63) in the K tile: the MFMA A row m of key block kb that
 // yields, in the accumulator layout, key g*32 + kb*16 + i in register i of lane half g.
@@ -117,15 +124,34 @@ __device__ __forceinline__ void scores(const uint8_t* __restrict__ kt, const Lan
 }
 
 // O^T += V^T P^T over 4 blocks of 32 channels; the row sum of P accumulates in rs.
+// D = A B 2^(sb - 127) + C: the B operand (P^T, one query per lane) scaled by the E8M0
+// exponent in byte 0 of sb; the A scale sa holds 127 (x1) in a register.
+__device__ __forceinline__ v16f mfma_pv(v8i a, v8i b, v16f c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+}
+
 __device__ __forceinline__ void pv(const uint8_t* __restrict__ vt, const Lane& ln, const v8i& p,
-                                   const v8i& ones, v16f& rs, v16f& o0, v16f& o1, v16f& o2,
-                                   v16f& o3) {
+                                   const v8i& ones, int sa, int sb, v16f& rs, v16f& o0,
+                                   v16f& o1, v16f& o2, v16f& o3) {
   const uint8_t* vr = vt + ln.n * kBN;
-  rs = mfma_e4m3_32x32x64(ones, p, rs);
-  o0 = mfma_e4m3_32x32x64(load32(vr + ln.vs0, vr + ln.vs1), p, o0);
-  o1 = mfma_e4m3_32x32x64(load32(vr + 32 * kBN + ln.vs0, vr + 32 * kBN + ln.vs1), p, o1);
-  o2 = mfma_e4m3_32x32x64(load32(vr + 64 * kBN + ln.vs0, vr + 64 * kBN + ln.vs1), p, o2);
-  o3 = mfma_e4m3_32x32x64(load32(vr + 96 * kBN + ln.vs0, vr + 96 * kBN + ln.vs1), p, o3);
+  rs = mfma_pv(ones, p, rs, sa, sb);
+  o0 = mfma_pv(load32(vr + ln.vs0, vr + ln.vs1), p, o0, sa, sb);
+  o1 = mfma_pv(load32(vr + 32 * kBN + ln.vs0, vr + 32 * kBN + ln.vs1), p, o1, sa, sb);
+  o2 = mfma_pv(load32(vr + 64 * kBN + ln.vs0, vr + 64 * kBN + ln.vs1), p, o2, sa, sb);
+  o3 = mfma_pv(load32(vr + 96 * kBN + ln.vs0, vr + 96 * kBN + ln.vs1), p, o3, sa, sb);
+}
+
+// Maxima of scores written as the instructions themselves: the scores are never NaN, and
+// fmaxf would make the compiler quiet every input first (one v_max_f32 x, x, x each).
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float vmax(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
 }
 
 // Maximum over the two lane halves (lanes l and l ^ 32 hold the two key halves of one
@@ -133,7 +159,7 @@ __device__ __forceinline__ void pv(const uint8_t* __restrict__ vt, const Lane& l
 __device__ __forceinline__ float half_swap_max(float mx) {
   const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
                                                    false, false);
-  return __builtin_fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+  return vmax(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
 }
 
 // Scores i0 .. i0+3 of one 16-score block -> 4 packed E4M3 weights exp2(s*c - mc). The
@@ -323,9 +349,9 @@ void attn_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__
   // ---- per-lane state for query n
   // ref_prev: reference exponent (the running row maximum in log2 units, rounded up to an
   // integer) after the last tile whose softmax ran; ref_acc: the exponent that the O and
-  // row-sum accumulators are relative to (they catch up at the top of each iteration,
-  // before the pending PV is issued, so the rescale never sits between the softmax and the
-  // MFMAs it overlaps). Both hold integers (as floats) or -inf before the first tile.
+  // row-sum accumulators are relative to (set at the first PV product, moved only when the
+  // shift to ref_prev would pass kMaxShift). Both hold integers (as floats) or -inf before
+  // the first tile.
   float ref_prev = -__builtin_inff();
   float ref_acc = -__builtin_inff();
   v16f o0 = {}, o1 = {}, o2 = {}, o3 = {};
@@ -334,6 +360,8 @@ void attn_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__
 #pragma unroll
   for (int r = 0; r < 8; ++r) ones[r] = (int)kOnesE4M3;
   asm volatile("" : "+v"(ones));   // opaque: kept in registers, not rebuilt every tile
+  int s127 = 127;                  // E8M0 1.0 for the A operand, from a register
+  asm volatile("" : "+v"(s127));
   const int last_lim = S - (ntiles - 1) * kBN;          // valid keys of the last tile
   v16f sa0, sa1, sb0, sb1;                              // two score register sets
   v8i p_prev;                                           // quantised P of the previous tile
@@ -343,8 +371,12 @@ void attn_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__
   loads_barrier<0>();
   scores(kst, ln, qb0, qb1, sa0, sa1);
 
-  auto catch_up = [&]() __attribute__((always_inline)) {
-    if (wave_any(ref_prev > ref_acc)) {
+  // The accumulators stay relative to ref_acc; the pending P is relative to ref_prev, so
+  // its PV and row-sum products are scaled by 2^(ref_prev - ref_acc) through the B scale of
+  // the MFMA (returned as the E8M0 byte). Only when that shift would pass kMaxShift (and on
+  // the first tile, ref_acc = -inf) are the accumulators rescaled to ref_prev.
+  auto catch_up = [&]() __attribute__((always_inline)) -> int {
+    if (wave_any(ref_prev - ref_acc > kMaxShift)) {
       // an exact power of two, 2^(ref_acc - ref_prev); 0 while ref_acc = -inf (the clamp
       // keeps the conversion to int defined)
       const float alpha = __builtin_ldexpf(1.0f, (int)__builtin_fmaxf(ref_acc - ref_prev, -200.0f));
@@ -353,8 +385,9 @@ void attn_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__
       o1 *= alpha;
       o2 *= alpha;
       o3 *= alpha;
+      ref_acc = ref_prev;
     }
-    ref_acc = ref_prev;
+    return 127 + (int)(ref_prev - ref_acc);
   };
 
   // Synchronisation of a pair of iterations t, t+1 (t odd). They read K(t+1), K(t+2),
@@ -370,14 +403,15 @@ void attn_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__
     load_v(t + 2);
   };
 
+
   // Iteration t < ntiles - 1: softmax of tile t (scores in cur), scores of tile t+1 into
   // nxt, PV of tile t-1 (when t > 0).
   auto iteration = [&](int t, v16f& cur0, v16f& cur1, v16f& nxt0, v16f& nxt1,
-                       auto do_pv) __attribute__((always_inline)) {
+                       auto do_pv, int sk, int sv) __attribute__((always_inline)) {
     constexpr bool PV = decltype(do_pv)::value;
-    const int sk = (t + 1) & (kStages - 1);     // stage of K(t+1)
-    const int sv = (t - 1) & (kStages - 1);     // stage of V(t-1)
-    if (PV) catch_up();
+    // sk: stage of K(t+1), sv: stage of V(t-1) (constants where the caller knows t mod 4)
+    int sb = 127;
+    if (PV) sb = catch_up();
     // ---- one region, written in issue order: each MFMA is followed by one chunk of the
     // softmax (a part of the row maximum, or the exp/convert of 4 scores), and
     // sched_barrier(0) keeps every pair where it is, so the matrix core always has the
@@ -394,30 +428,32 @@ void attn_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__
       va3 = load32(vr + 96 * kBN + ln.vs0, vr + 96 * kBN + ln.vs1);
     }
     __builtin_amdgcn_sched_barrier(0);
-    if (PV) rs = mfma_e4m3_32x32x64(ones, p_prev, rs);
-    float mx = __builtin_fmaxf(cur0[0], cur0[1]);
+    if (PV) rs = mfma_pv(ones, p_prev, rs, s127, sb);
+    float mx = vmax3(cur0[0], cur0[1], cur0[2]);
 #pragma unroll
-    for (int i = 2; i < 16; ++i) mx = __builtin_fmaxf(mx, cur0[i]);
+    for (int i = 3; i < 15; i += 2) mx = vmax3(mx, cur0[i], cur0[i + 1]);
     __builtin_amdgcn_sched_barrier(0);
-    if (PV) o0 = mfma_e4m3_32x32x64(va0, p_prev, o0);
+    if (PV) o0 = mfma_pv(va0, p_prev, o0, s127, sb);
     const v8i ka0 = load32(kr0 + ln.ks00, kr0 + ln.ks01);
     const v8i kb0 = load32(kr1 + ln.ks00, kr1 + ln.ks01);
     const v8i ka1 = load32(kr0 + ln.ks10, kr0 + ln.ks11);
     const v8i kb1 = load32(kr1 + ln.ks10, kr1 + ln.ks11);
+    mx = vmax3(mx, cur0[15], cur1[0]);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) mx = __builtin_fmaxf(mx, cur1[i]);
+    for (int i = 1; i < 15; i += 2) mx = vmax3(mx, cur1[i], cur1[i + 1]);
+    mx = vmax(mx, cur1[15]);
     // c > 0, so the maximum of the raw dot products gives the maximum score
-    const float ref_cur = __builtin_fmaxf(ref_prev, __builtin_ceilf(half_swap_max(mx) * c));
+    const float ref_cur = vmax(ref_prev, __builtin_ceilf(half_swap_max(mx) * c));
     const float mc = ref_cur - kLog2E4M3Max;
     __builtin_amdgcn_sched_barrier(0);
     v8i p;
-    if (PV) o1 = mfma_e4m3_32x32x64(va1, p_prev, o1);
+    if (PV) o1 = mfma_pv(va1, p_prev, o1, s127, sb);
     p[0] = quant4(cur0, 0, c, mc);
     __builtin_amdgcn_sched_barrier(0);
-    if (PV) o2 = mfma_e4m3_32x32x64(va2, p_prev, o2);
+    if (PV) o2 = mfma_pv(va2, p_prev, o2, s127, sb);
     p[1] = quant4(cur0, 4, c, mc);
     __builtin_amdgcn_sched_barrier(0);
-    if (PV) o3 = mfma_e4m3_32x32x64(va3, p_prev, o3);
+    if (PV) o3 = mfma_pv(va3, p_prev, o3, s127, sb);
     p[2] = quant4(cur0, 8, c, mc);
     __builtin_amdgcn_sched_barrier(0);
     nxt0 = mfma_e4m3_32x32x64(ka0, qb0, zero16);
@@ -444,19 +480,29 @@ void attn_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__
   // 0 reads only prologue tiles, which the barrier above published.
   int t = 0;
   if (ntiles > 1) {
-    iteration(0, sa0, sa1, sb0, sb1, F_{});
+    iteration(0, sa0, sa1, sb0, sb1, F_{}, 1, 3);
     t = 1;
-    for (; t + 2 < ntiles; t += 2) {
+    // two pairs per trip, t = 1 (mod 4): every ring stage is a constant
+    for (; t + 4 < ntiles; t += 4) {
       pair_sync(t);
-      iteration(t, sb0, sb1, sa0, sa1, T_{});
-      iteration(t + 1, sa0, sa1, sb0, sb1, T_{});
+      iteration(t, sb0, sb1, sa0, sa1, T_{}, 2, 0);
+      iteration(t + 1, sa0, sa1, sb0, sb1, T_{}, 3, 1);
+      pair_sync(t + 2);
+      iteration(t + 2, sb0, sb1, sa0, sa1, T_{}, 0, 2);
+      iteration(t + 3, sa0, sa1, sb0, sb1, T_{}, 1, 3);
+    }
+    if (t + 2 < ntiles) {
+      pair_sync(t);
+      iteration(t, sb0, sb1, sa0, sa1, T_{}, 2, 0);
+      iteration(t + 1, sa0, sa1, sb0, sb1, T_{}, 3, 1);
+      t += 2;
     }
     if (t + 1 < ntiles) {
       // a last single iteration t = ntiles - 2: K(t+1), V(t-1) came with the previous
       // pair; V(t+1) = V(ntiles-1) is still to load (for the epilogue)
       loads_barrier<0>();
       load_v(t + 1);
-      iteration(t, sb0, sb1, sa0, sa1, T_{});
+      iteration(t, sb0, sb1, sa0, sa1, T_{}, (t + 1) & 3, (t - 1) & 3);
       ++t;
     } else {
       sa0 = sb0;   // the last tile's scores are in set b: move them (once)
@@ -466,8 +512,8 @@ void attn_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__
   // ---- epilogue: t = ntiles - 1, scores in set a; V(ntiles-2), V(ntiles-1) loaded
   loads_barrier<0>();
   if (ntiles > 1) {
-    catch_up();
-    pv(vst + ((ntiles - 2) & (kStages - 1)) * kVTileBytes, ln, p_prev, ones, rs, o0, o1, o2,
+    const int sb = catch_up();
+    pv(vst + ((ntiles - 2) & (kStages - 1)) * kVTileBytes, ln, p_prev, ones, s127, sb, rs, o0, o1, o2,
        o3);   // PV(ntiles-2)
   }
   {
@@ -480,8 +526,8 @@ void attn_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__
                     : quantise_p<false>(sa0, sa1, c, mc, ln.g, kBN);
     ref_prev = ref_cur;
   }
-  catch_up();
-  pv(vst + ((ntiles - 1) & (kStages - 1)) * kVTileBytes, ln, p_prev, ones, rs, o0, o1, o2,
+  const int sb_last = catch_up();
+  pv(vst + ((ntiles - 1) & (kStages - 1)) * kVTileBytes, ln, p_prev, ones, s127, sb_last, rs, o0, o1, o2,
      o3);   // PV(ntiles-1)
 
   // ---- O = O * scale_v / l, bf16, one query row per lane
