@@ -49,8 +49,9 @@
 //     roles without copies, and every LDS ring stage the operand reads use is a constant
 //     (an immediate offset, no address arithmetic per tile); a ragged last tile is handled
 //     (masked) only in the epilogue;
-//   * the row maximum is a chain of v_max3 written as the instruction itself (fmaxf would
-//     make the compiler quiet every score first; scores are never NaN);
+//   * the row maximum is a tree of v_max3 (depth 4 over a lane's 32 scores) written as
+//     the instruction itself (fmaxf would make the compiler quiet every score first;
+//     scores are never NaN);
 //   * K and V8t tiles go global -> LDS with buffer loads that write LDS directly (no VGPR
 //     staging, no ds_write), in four-stage rings; tiles move in pairs, with one vmcnt wait
 //     and one barrier per pair of tiles, each pair's loads issued one pair ahead of use;
@@ -429,19 +430,21 @@ void attn_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__
     }
     __builtin_amdgcn_sched_barrier(0);
     if (PV) rs = mfma_pv(ones, p_prev, rs, s127, sb);
-    float mx = vmax3(cur0[0], cur0[1], cur0[2]);
-#pragma unroll
-    for (int i = 3; i < 15; i += 2) mx = vmax3(mx, cur0[i], cur0[i + 1]);
+    const float mx0 = vmax(vmax3(vmax3(cur0[0], cur0[1], cur0[2]), vmax3(cur0[3], cur0[4], cur0[5]),
+                                 vmax3(cur0[6], cur0[7], cur0[8])),
+                           vmax3(vmax3(cur0[9], cur0[10], cur0[11]),
+                                 vmax3(cur0[12], cur0[13], cur0[14]), cur0[15]));
     __builtin_amdgcn_sched_barrier(0);
     if (PV) o0 = mfma_pv(va0, p_prev, o0, s127, sb);
     const v8i ka0 = load32(kr0 + ln.ks00, kr0 + ln.ks01);
     const v8i kb0 = load32(kr1 + ln.ks00, kr1 + ln.ks01);
     const v8i ka1 = load32(kr0 + ln.ks10, kr0 + ln.ks11);
     const v8i kb1 = load32(kr1 + ln.ks10, kr1 + ln.ks11);
-    mx = vmax3(mx, cur0[15], cur1[0]);
-#pragma unroll
-    for (int i = 1; i < 15; i += 2) mx = vmax3(mx, cur1[i], cur1[i + 1]);
-    mx = vmax(mx, cur1[15]);
+    const float mx1 = vmax(vmax3(vmax3(cur1[0], cur1[1], cur1[2]), vmax3(cur1[3], cur1[4], cur1[5]),
+                                 vmax3(cur1[6], cur1[7], cur1[8])),
+                           vmax3(vmax3(cur1[9], cur1[10], cur1[11]),
+                                 vmax3(cur1[12], cur1[13], cur1[14]), cur1[15]));
+    const float mx = vmax(mx0, mx1);
     // c > 0, so the maximum of the raw dot products gives the maximum score
     const float ref_cur = vmax(ref_prev, __builtin_ceilf(half_swap_max(mx) * c));
     const float mc = ref_cur - kLog2E4M3Max;

@@ -7,12 +7,14 @@
 // converter would turn values beyond 464 into NaN), then the hardware RNE converter.
 //
 // Work split (grid-stride, so the grid stays small whatever the batch): blocks
-// [0, nb_qk) stream Q and K element-wise into [T][H][D] (four 16-byte groups in flight
-// per thread); blocks [nb_qk, nb_qk + nb_v) each take a contiguous run of (128-column
-// tile, head) pairs of the padded key axis of V8t [H][D][Tp] (see fp8attn.h), so the
-// sequence that holds a tile is found once per run and then stepped; each pair loads 128
-// tokens x 128 channels of V, quantises, transposes through LDS and writes 128 channel
-// rows of 128 contiguous key bytes. Columns outside every sequence are written as 0 so the attention
+// [0, nb_qk) stream Q and K element-wise into [T][H][D] (two groups of 16 elements in
+// flight per thread, each 32 bytes read and 16 written at once); blocks
+// [nb_qk, nb_qk + nb_v) each take a contiguous run of (head, 128-column tile) pairs of the
+// padded key axis of V8t [H][D][Tp] (see fp8attn.h), the tiles of one head consecutive,
+// so that a block's successive tiles extend the same V8t rows and the sequence that holds
+// a tile is found once per run and head and then stepped; each pair loads 128 tokens x 128
+// channels of V, quantises, transposes through LDS and writes 128 channel rows of 128
+// contiguous key bytes. Columns outside every sequence are written as 0 so the attention
 // kernel can read whole tiles without bounds checks on V.
 //
 // Three modes share that kernel:
@@ -35,7 +37,7 @@ namespace fp8attn {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kQkGroups = 4;                                    // 8-element groups per thread step
+constexpr int kQkGroups = 2;                                    // 16-element groups per thread step
 constexpr int kVTile = 128;                                     // keys per V tile
 constexpr int kLdsRow = kVTile + 16;                            // bytes per LDS row (16B aligned)
 constexpr int kMaxBlocksPerPart = 1024;                         // Q/K blocks, V blocks
@@ -118,33 +120,37 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
   if ((int)blockIdx.x < nb_qk) {
     // ---- Q and K: element-wise stream over the concatenation [Q | K] of 2n elements
     if (MODE == kRedo && !work[0] && !work[1]) return;
-    const int64_t groups = 2 * n / 8;                 // n is a multiple of 128
+    const int64_t groups = 2 * n / 16;                // n is a multiple of 128
     const int64_t step = (int64_t)nb_qk * kThreads * kQkGroups;
     uint32_t mq = 0, mk = 0;
     for (int64_t g0 = (int64_t)blockIdx.x * kThreads * kQkGroups; g0 < groups; g0 += step) {
-      uint4 r[kQkGroups];
+      uint4 r[kQkGroups][2];
 #pragma unroll
       for (int u = 0; u < kQkGroups; ++u) {
         const int64_t g = g0 + u * kThreads + tid;
         if (g < groups) {
-          const int64_t e = g * 8;
+          const int64_t e = g * 16;
           const bool is_k = e >= n;
-          r[u] = *reinterpret_cast<const uint4*>((is_k ? k : q) + (is_k ? e - n : e));
+          const uint4* p = reinterpret_cast<const uint4*>((is_k ? k : q) + (is_k ? e - n : e));
+          r[u][0] = p[0];
+          r[u][1] = p[1];
         }
       }
 #pragma unroll
       for (int u = 0; u < kQkGroups; ++u) {
         const int64_t g = g0 + u * kThreads + tid;
         if (g < groups) {
-          const int64_t e = g * 8;
+          const int64_t e = g * 16;
           const bool is_k = e >= n;
           if (MODE == kObserve) {
-            if (is_k) mk = absmax8(mk, r[u]);
-            else mq = absmax8(mq, r[u]);
+            if (is_k) mk = absmax8(absmax8(mk, r[u][0]), r[u][1]);
+            else mq = absmax8(absmax8(mq, r[u][0]), r[u][1]);
           }
           if (MODE != kRedo || work[is_k ? 1 : 0]) {
-            const uint2 o = quant8(r[u], inv[is_k ? 1 : 0]);
-            *reinterpret_cast<uint2*>((is_k ? k8 : q8) + (is_k ? e - n : e)) = o;
+            const uint2 a = quant8(r[u][0], inv[is_k ? 1 : 0]);
+            const uint2 b = quant8(r[u][1], inv[is_k ? 1 : 0]);
+            *reinterpret_cast<uint4*>((is_k ? k8 : q8) + (is_k ? e - n : e)) =
+                make_uint4(a.x, a.y, b.x, b.y);
           }
         }
       }
@@ -156,8 +162,8 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
     return;
   }
 
-  // ---- V: (padded key tile, head) pairs; each block takes a contiguous run of them, in
-  // which the key tile -- and so the sequence -- only moves forward
+  // ---- V: (head, padded key tile) pairs; each block takes a contiguous run of them, in
+  // which, within one head, the key tile -- and so the sequence -- only moves forward
   if (MODE == kRedo && !work[2]) return;
   const float inv_v = inv[2];
   const int64_t tiles = (Tp / kVTile) * H;
@@ -169,8 +175,10 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
   uint32_t mv = 0;
   int seq = -1;
   for (int64_t vb = vb_begin; vb < vb_end; ++vb) {
-    const int h = (int)(vb % H);
-    const int64_t col0 = (vb / H) * kVTile;          // first padded key column of the tile
+    const int64_t ntile = Tp / kVTile;
+    const int h = (int)(vb / ntile);
+    const int64_t col0 = (vb % ntile) * kVTile;      // first padded key column of the tile
+    if (col0 == 0) seq = -1;                         // a new head: search again
     // sequence whose padded region holds col0: the largest i with pad_start(i) <= col0
     // (starts increase strictly); a binary search for the run's first tile, then steps
     if (seq < 0) {
@@ -237,7 +245,7 @@ hipError_t launch_mode(fp8attn_state* st, const uint16_t* q, const uint16_t* k,
                        const uint16_t* v, const int32_t* cu, int num_seqs, int64_t T, int H,
                        uint8_t* q8, uint8_t* k8, uint8_t* v8t, int64_t Tp, hipStream_t s) {
   const int64_t n = T * H * kHeadDim;
-  const int64_t per_block = (int64_t)kThreads * kQkGroups * 8;
+  const int64_t per_block = (int64_t)kThreads * kQkGroups * 16;
   int64_t nb_qk = (2 * n + per_block - 1) / per_block;
   // the re-quantise pass keeps the full grid: when it works (the first forward of a layer,
   // or a new window maximum -- with amax varying between forwards, one of Q/K/V does so in
