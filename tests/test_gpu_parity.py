@@ -355,6 +355,48 @@ def test_explicit_softmax_scale(sm):
     _assert_close("bf16 vs oracle", bf16_to_f64(bout), oracle_ref_rows(q, k, v, cu, sm32))
 
 
+@pytest.mark.parametrize("sm", [1.0, 0.43])
+def test_reference_exponent_jump_past_the_shift_limit(sm):
+    # every query lies close to u, the other keys are small and key 100 equals u: the row
+    # maximum jumps by about |u|^2 sm log2 e (185 log2 units at sm = 1, 80 at 0.43) after
+    # the first key tile, past the 2^64 that the kernel applies through the MFMA's operand
+    # scale, so its accumulators are rescaled instead (to 0 at sm = 1, by about 2^-80 at
+    # 0.43); key 250 (0.95 u, a later tile) keeps a weight of its own beside key 100
+    S, H = 300, 2
+    g = torch.Generator().manual_seed(101)
+    u = torch.randn(H, 128, generator=g)
+    u = u * (128.0 / (u * u).sum(dim=1, keepdim=True)).sqrt()        # |u|^2 = 128 per head
+    q = u[None] + 0.1 * torch.randn(S, H, 128, generator=g)
+    k = 0.01 * torch.randn(S, H, 128, generator=g)
+    k[100] = u
+    k[250] = 0.95 * u
+    v = torch.randn(S, H, 128, generator=g)
+    q, k, v = (x.to(torch.bfloat16).to(DEV) for x in (q, k, v))
+    cu = [0, S]
+    say(f"reference jump: S={S} H={H} softmax scale {sm}")
+    sm32 = float(np.float32(sm))
+    sc = [oracle.scale_pair(a) for a in _amax3(q, k, v)]
+    # the premise, from the E4M3 codes: every row's maximum lies more than 64 log2 units
+    # above the maximum of its first 64 keys, and key 250 keeps a nonzero weight
+    luts = [quant_lut(x[1]) for x in sc]
+    q8, k8, v8 = (lut[bits(x)] for lut, x in zip(luts, (q, k, v)))
+    for h in range(H):
+        _, p8, _ = oracle.fp8_attention_head(q8[:, h], k8[:, h], v8[:, h], sc[0][0], sc[1][0],
+                                             sc[2][0], sm32, return_weights=True)
+        t = (oracle.e4m3_decode(q8[:, h]) @ oracle.e4m3_decode(k8[:, h]).T
+             * (sc[0][0] * sc[1][0] * sm32 / math.log(2.0)))
+        assert np.all(t.max(axis=1) - t[:, :64].max(axis=1) > 64.0)
+        assert np.all(p8[:, 250] > 0) and np.all(p8[:, :64] == 0)
+    out, _ = _run_fp8(q, k, v, cu, softmax_scale=sm)
+    got, want = bf16_to_f64(out), oracle_fp8_rows(q, k, v, cu, sc, sm32)
+    # two keys carry every row with scores of 55-128 nats, so the matrix core's score error
+    # (relative to the largest product) moves key 250's weight across E4M3 midpoints in
+    # more rows than at unit variance: the cap of the large-score regime
+    st = check_rows(got, want, 1.0, _bound_fn(q, k, v, cu, sc, sm32), cap=OVER_TOL_CAP_OUTLIERS)
+    say(f"  fp8 vs oracle: {st}")
+    assert st["ok"], st
+
+
 def test_two_layers_on_two_streams_concurrently():
     # the library keeps no global state: two layers, each with its own state and workspace,
     # running three dynamic forwards at once on two streams give the outputs and states
