@@ -49,6 +49,9 @@
 //     roles without copies, and every LDS ring stage the operand reads use is a constant
 //     (an immediate offset, no address arithmetic per tile); a ragged last tile is handled
 //     (masked) only in the epilogue;
+//   * the wave's issue priority is raised from its first MFMA of an iteration to its
+//     last, so that of the two waves on a SIMD the one with MFMAs still to issue gets the
+//     vector ALU first (3-5 % faster than equal priority);
 //   * the row maximum is a tree of v_max3 (depth 4 over a lane's 32 scores) written as
 //     the instruction itself (fmaxf would make the compiler quiet every score first;
 //     scores are never NaN);
@@ -429,6 +432,10 @@ void attn_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__
       va3 = load32(vr + 96 * kBN + ln.vs0, vr + 96 * kBN + ln.vs1);
     }
     __builtin_amdgcn_sched_barrier(0);
+    // raised issue priority from the first MFMA to the last: of the two waves on a SIMD,
+    // the one with MFMAs left to issue gets the vector ALU for the chunks between them,
+    // and the one in its MFMA-free tail (two chunks, the loop's bookkeeping) yields
+    __builtin_amdgcn_s_setprio(1);
     if (PV) rs = mfma_pv(ones, p_prev, rs, s127, sb);
     const float mx0 = vmax(vmax3(vmax3(cur0[0], cur0[1], cur0[2]), vmax3(cur0[3], cur0[4], cur0[5]),
                                  vmax3(cur0[6], cur0[7], cur0[8])),
@@ -469,6 +476,7 @@ void attn_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__
     p[5] = quant4(cur1, 4, c, mc);
     __builtin_amdgcn_sched_barrier(0);
     nxt1 = mfma_e4m3_32x32x64(kb1, qb1, nxt1);
+    __builtin_amdgcn_s_setprio(0);
     p[6] = quant4(cur1, 8, c, mc);
     __builtin_amdgcn_sched_barrier(0);
     p[7] = quant4(cur1, 12, c, mc);
