@@ -294,6 +294,9 @@ void attn_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
       for (int cb = 0; cb < 4; ++cb) va[cb] = ldsv(sv, cb, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
+    // raised issue priority while the iteration's MFMAs issue: of the two waves on a SIMD,
+    // the one with matrix-core work pending gets the vector ALU for the chunks between them
+    __builtin_amdgcn_s_setprio(1);
     if (PV) {
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) vb[cb] = ldsv(sv, cb, 1);
@@ -377,6 +380,7 @@ void attn_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    __builtin_amdgcn_s_setprio(0);
     pin(p);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) p_prev[ks] = p[ks];
