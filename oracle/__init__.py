@@ -15,8 +15,11 @@ and, for the number format, the OCP 8-bit floating point specification (E4M3).
 
 Parity status: every function here is pinned by CPU tests (tests/test_oracle_*.py)
 against closed forms, exhaustive brute force, a library codec or the pages' worked
-values -- except the exact bit pattern of an attention output, for which no page prints
-a value ("parity unpinned" for that one quantity; it is pinned through invariants).
+values. No page prints an attention output, so the attention functions are pinned by a
+two-key case worked out by hand (its weights 320 and 128 and sum 448), a pure-Python
+brute force of the rule on tiny batches, invariants (a zero query gives the mean of V, a
+constant V comes out unchanged, key order does not matter, the largest weight lies in
+[224, 448]) and a mutation check that each plausible slip fails one of these.
 """
 
 from .e4m3 import (E4M3_MAX, e4m3_decode, e4m3_encode, e4m3_decode_table,
